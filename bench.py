@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-Toeplitz FFT matvec on one MI355X.
+
+One step = one F apply followed by one F* apply (all five stages of each,
+"Mixed-precision FFTMatvec performance optimization on AMD GPUs", section
+1.1) at Nm=5000, Nd=100, Nt=1000 in the page's mixed precision (section 2.2:
+F with FFT + SBGEMV in FP32, F* with SBGEMV + IFFT in FP32), inputs resident
+in HBM. Prints one JSON line.
+
+value = algorithmic HBM bytes of the step / step time (GB/s). The bytes are
+the fused minimum of each apply: read the FP64 input once, write and read
+the stage-2 output once, read Fhat once, write and read the stage-3 output
+once, write the FP64 output once (zero padding not counted).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--shape", default="main", choices=["tiny", "small", "main", "scale"])
+    ap.add_argument("--mask", type=lambda s: int(s, 0), default=0x186)
+    ap.add_argument("--staged", action="store_true", help="five-kernel form (pad/unpad materialised)")
+    ap.add_argument("--kernel-reps", type=int, default=20, help="stage-3-only launches timed for the roofline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-cols", type=int, default=0, help="oracle sample: input columns (0 = Nm/5)")
+    ap.add_argument("--no-check", action="store_true", help="skip the spot-step check against the oracle")
+    return ap.parse_args()
+
+
+def elem(mask, direction, s1, s2, cplx):
+    f32 = bool(mask & (1 << (5 * direction + s1 - 1))) or bool(mask & (1 << (5 * direction + s2 - 1)))
+    return (8 if f32 else 16) if cplx else (4 if f32 else 8)
+
+
+def apply_bytes(Nm, Nd, Nt, mask, direction):
+    """Fused-minimum algorithmic bytes of one apply."""
+    K = Nt + 1
+    nin, nout = (Nm, Nd) if direction == 0 else (Nd, Nm)
+    fhat = K * Nd * Nm * (8 if mask & (1 << (5 * direction + 2)) else 16)
+    hin = K * nin * elem(mask, direction, 2, 3, True)
+    hout = K * nout * elem(mask, direction, 3, 4, True)
+    return Nt * nin * 8 + 2 * hin + fhat + 2 * hout + Nt * nout * 8
+
+
+def sbgemv_bytes(Nm, Nd, Nt, mask, direction):
+    """Algorithmic bytes of one stage-3 launch: Fhat + its input + its output."""
+    K = Nt + 1
+    nin, nout = (Nm, Nd) if direction == 0 else (Nd, Nm)
+    fhat = K * Nd * Nm * (8 if mask & (1 << (5 * direction + 2)) else 16)
+    return fhat + K * nin * elem(mask, direction, 2, 3, True) + K * nout * elem(mask, direction, 3, 4, True)
+
+
+def cpu_baseline(shape, mask, F, m, d, cols):
+    """The FP64 CPU oracle (as it stands) on a column sample of the same
+    workload: Nm reduced to `cols`, everything else unchanged. One F and one
+    F* apply with Fhat precomputed, median of 3; scaled to the full step by
+    the byte model."""
+    import oracle
+
+    Nm, Nd, Nt = shape.Nm, shape.Nd, shape.Nt
+    Fs = np.ascontiguousarray(F[:, :, :cols])
+    ms = np.ascontiguousarray(m[:, :cols])
+    Fh = oracle.setup(Fs)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.apply(Fh, ms)
+        oracle.apply_adjoint(Fh, d)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    sample_bytes = apply_bytes(cols, Nd, Nt, mask, 0) + apply_bytes(cols, Nd, Nt, mask, 1)
+    gbs = sample_bytes / t / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"F and F* apply at Nm={cols} (of {Nm}), Nd={Nd}, Nt={Nt}, FP64 oracle, Fhat precomputed, "
+                      f"median of 3: {t * 1e3:.1f} ms; GB/s on the step's byte model at that Nm",
+            "ms_per_step_full_equiv": round(t * 1e3 * Nm / cols, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fft_block_toeplitz_amd as fm
+    from fft_block_toeplitz_amd import workloads as W
+
+    shape = W.SHAPES[args.shape]
+    Nm, Nd, Nt, mask = shape.Nm, shape.Nd, shape.Nt, args.mask
+    t0 = time.perf_counter()
+    F, m, d = W.problem(shape)
+    gen_s = time.perf_counter() - t0
+    print(f"[bench] inputs {args.shape} Nm={Nm} Nd={Nd} Nt={Nt} generated in {gen_s:.1f}s", file=sys.stderr,
+          flush=True)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    F_dev = torch.from_numpy(F).to(dev)
+    m_dev = torch.from_numpy(m).to(dev)
+    d_dev = torch.from_numpy(d).to(dev)
+    flags = fm.FFTMV_FLAG_STAGED if args.staged else 0
+    t0 = time.perf_counter()
+    plan = fm.Plan(F_dev, mask | flags)
+    setup_s = time.perf_counter() - t0
+    del F_dev
+    torch.cuda.empty_cache()
+    v_dev = torch.empty((Nt, Nd), dtype=torch.float64, device=dev)
+    w_dev = torch.empty((Nt, Nm), dtype=torch.float64, device=dev)
+    print(f"[bench] setup {setup_s:.2f}s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        plan.apply(m_dev, out=v_dev)
+        plan.apply_adjoint(d_dev, out=w_dev)
+    torch.cuda.synchronize()
+
+    # whole steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps + 1)]
+    t_wall = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        plan.apply(m_dev, out=v_dev)
+        ev[3 * i + 1].record(stream)
+        plan.apply_adjoint(d_dev, out=w_dev)
+        ev[3 * i + 2].record(stream)
+        ev[3 * i + 3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = ev[0].elapsed_time(ev[3 * args.steps])
+    f_ms = [ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(args.steps)]
+    a_ms = [ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(args.steps)]
+    ms_step = total_ms / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f}s)", file=sys.stderr, flush=True)
+
+    bF, bA = apply_bytes(Nm, Nd, Nt, mask, 0), apply_bytes(Nm, Nd, Nt, mask, 1)
+    value = (bF + bA) / (ms_step * 1e-3) / 1e9
+
+    # dominant kernel: stage 3 of F alone (same kernel and launch as in the
+    # apply), timed with events on the stream it is launched on
+    kernel = {}
+    for direction, name in ((0, "sbgemv_n"), (1, "sbgemv_c")):
+        plan.run_stages(direction, 3, 3)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.kernel_reps):
+            plan.run_stages(direction, 3, 3)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kms = e0.elapsed_time(e1) / args.kernel_reps
+        kb = sbgemv_bytes(Nm, Nd, Nt, mask, direction)
+        kernel[name] = {"avg_ms": round(kms, 5), "bytes": kb, "GB/s": round(kb / (kms * 1e-3) / 1e9, 1)}
+    print(f"[bench] kernels {kernel}", file=sys.stderr, flush=True)
+
+    # correctness spot check against the oracle (direct sum at a few steps)
+    check = None
+    if not args.no_check:
+        import oracle
+
+        steps = np.array([0, 1, Nt // 2, Nt - 1])
+        plan.apply(m_dev, out=v_dev)
+        plan.apply_adjoint(d_dev, out=w_dev)
+        torch.cuda.synchronize()
+        v, w = v_dev.cpu().numpy(), w_dev.cpu().numpy()
+        check = {"steps": steps.tolist(),
+                 "rel_err_F": float(oracle.rel_l2(v[steps], oracle.direct(F, m, steps))),
+                 "rel_err_Fadj": float(oracle.rel_l2(w[steps], oracle.direct_adjoint(F, d, steps)))}
+        print(f"[bench] spot check {check}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cols = args.cpu_sample_cols or max(1, Nm // 5)
+        t0 = time.perf_counter()
+        cpu = cpu_baseline(shape, mask, F, m, d, cols)
+        print(f"[bench] cpu baseline {cpu} ({time.perf_counter() - t0:.1f}s)", file=sys.stderr, flush=True)
+
+    kn = kernel["sbgemv_n"]
+    achieved = kn["bytes"] / (kn["avg_ms"] * 1e-3) / 1e9
+    fmed, amed = float(np.median(f_ms)), float(np.median(a_ms))
+    out = {
+        "metric": "F / F* apply ms + HBM GB/s (% of peak) at Nm=5000 Nd=100 Nt=1000, mixed",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+f64",
+        "data": "synthetic",
+        "config": {"workload": f"FFT block-Toeplitz matvec, F + F* apply, Nm={Nm} Nd={Nd} Nt={Nt}, "
+                               f"precision mask {mask:#05x}" + (" (five-kernel form)" if args.staged else ""),
+                   "Nm": Nm, "Nd": Nd, "Nt": Nt, "mask": hex(mask), "staged": args.staged, "seed": 0},
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 1),
+        "f_apply_ms": round(fmed, 4),
+        "fadj_apply_ms": round(amed, 4),
+        "f_apply_GBs": round(bF / (fmed * 1e-3) / 1e9, 1),
+        "fadj_apply_GBs": round(bA / (amed * 1e-3) / 1e9, 1),
+        "bytes_per_step": bF + bA,
+        "kernels": kernel,
+        "roofline": {"bound": "hbm", "kernel": "sbgemv_n (stage 3, F)", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "check": check,
+        "context": {"page_mi355x_f_apply_ms": {"fp64": 1.9, "mixed": 1.3}},
+        "setup_s": round(setup_s, 3),
+    }
+    print(json.dumps(out), flush=True)
+    plan.close()
+
+
+if __name__ == "__main__":
+    main()

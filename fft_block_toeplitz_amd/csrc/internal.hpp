@@ -1,0 +1,87 @@
+// Host-side interface between the plan code and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace fftmv {
+
+constexpr int kMaxPasses = 24;
+constexpr int kMaxLds = 65536;  // bytes of LDS one FFT workgroup may use
+constexpr int kMaxChannelsPerBlock = 32;
+
+// Stockham radix schedule of the length-L complex FFT that carries the
+// length-2L real FFT (even samples in the real part, odd in the imaginary).
+struct FftGeom {
+  int L = 0;        // complex length (= Nt)
+  int npass = 0;
+  int radix[kMaxPasses] = {};
+  int ns[kMaxPasses] = {};      // product of the radices before this pass
+  int twstep[kMaxPasses] = {};  // 2L / (ns * radix): exponent step in the w_{2L} table
+};
+
+// Batched forward real FFT: nchan channels of Nt real samples (implicitly
+// zero-padded to 2 Nt), channel ch at src[t * src_ld + ch]; writes the Nt+1
+// bins of channel ch at dst + k * fstride + (ch / cpr) * ldr + ch % cpr, in
+// complex64 (dst32) and/or complex128 (dst64).
+struct FwdFftArgs {
+  int64_t Nt = 0, nchan = 0;
+  const void *src = nullptr;
+  int64_t src_ld = 0;
+  bool src_f32 = false;     // source holds float (else double)
+  bool round_f32 = false;   // round double samples to binary32 before use
+  void *dst32 = nullptr, *dst64 = nullptr;
+  int64_t fstride32 = 0, ldr32 = 0, fstride64 = 0, ldr64 = 0, cpr = 1;
+};
+
+// Batched inverse real FFT + unpad: bins k = 0..Nt of channel ch at
+// src[k * src_ld + ch] (complex); writes time steps 0..Nt-1 at
+// dst[t * dst_ld + ch] as float (dst_f32) or double.
+struct InvFftArgs {
+  int64_t Nt = 0, nchan = 0;
+  const void *src = nullptr;
+  int64_t src_ld = 0;
+  bool src_f32 = false;
+  void *dst = nullptr;
+  int64_t dst_ld = 0;
+  bool dst_f32 = false;
+  bool round_f32 = false;  // round to binary32 before a double store
+};
+
+// Per-frequency complex GEMV over Fhat [K][Nd][ldF].
+struct SbgemvArgs {
+  int64_t K = 0, Nd = 0, Nm = 0;
+  const void *F = nullptr;  // complex64 or complex128, per compute precision
+  int64_t ldF = 0;          // complex elements per row (even for complex64)
+  const void *x = nullptr;  // input  [K][ldx] complex (float if x_f32)
+  int64_t ldx = 0;
+  bool x_f32 = false;
+  void *y = nullptr;        // output [K][ldy] complex (float if y_f32)
+  int64_t ldy = 0;
+  bool y_f32 = false;
+};
+
+// Real [rows][cols] copy with precision change: dst[r*ldd+c] = src[r*lds+c].
+struct CastArgs {
+  int64_t rows = 0, cols = 0;
+  const void *src = nullptr;
+  int64_t lds = 0;
+  bool src_f32 = false;
+  void *dst = nullptr;
+  int64_t ldd = 0;
+  bool dst_f32 = false;
+};
+
+// Channels per FFT workgroup for this schedule, precision and batch size
+// (power of two, fits LDS and the per-thread butterfly budget); 0 if none.
+int fft_channels_per_block(const FftGeom &g, bool f32, int64_t nchan);
+
+hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
+                              hipStream_t s);
+hipError_t launch_fft_inverse(const FftGeom &g, const InvFftArgs &a, bool compute_f32, const void *tw,
+                              hipStream_t s);
+hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s);
+hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s);
+hipError_t launch_cast(const CastArgs &a, hipStream_t s);
+
+}  // namespace fftmv

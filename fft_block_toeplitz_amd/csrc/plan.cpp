@@ -1,0 +1,521 @@
+// Host side of the fftmv C ABI: plan construction, precision-mask dispatch
+// and the launch sequence of the five stages of "Mixed-precision FFTMatvec
+// performance optimization on AMD GPUs", section 1.1 (sections 1.2 and 2.2
+// for the adjoint and the per-stage precision choice).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "fftmv.h"
+#include "internal.hpp"
+
+using namespace fftmv;
+
+namespace {
+
+constexpr int kVersion = (0 << 16) | (1 << 8) | 0;
+
+// Buffers between stages: stage s of direction dir writes buf[dir][s].
+struct StageBuf {
+  void *p = nullptr;
+  int64_t ld = 0;  // elements per row
+};
+
+}  // namespace
+
+struct fftmv_plan_s {
+  int device = 0;
+  int64_t Nm = 0, Nd = 0, Nt = 0, K = 0;
+  uint32_t prec = 0, flags = 0;
+  FftGeom geom;
+  void *fhat32 = nullptr, *fhat64 = nullptr;
+  int64_t ldF32 = 0, ldF64 = 0;
+  void *tw32 = nullptr, *tw64 = nullptr;
+  StageBuf buf[2][5];
+  size_t fhat_bytes = 0, ws_bytes = 0;
+  void *allocs[16] = {};
+  int nalloc = 0;
+};
+
+namespace {
+
+bool fp32(uint32_t prec, int dir, int stage) { return (prec >> (5 * dir + stage - 1)) & 1u; }
+
+// complex64 rows are padded to an even length so that 16-byte vectors of two
+// entries never straddle rows
+int64_t padded_ld(int64_t n) { return (n + 1) & ~int64_t(1); }
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
+
+int status_from_hip(hipError_t e) {
+  if (e == hipSuccess) return FFTMV_SUCCESS;
+  if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return FFTMV_ERR_OUT_OF_MEMORY;
+  return FFTMV_ERR_HIP;
+}
+
+#define FFTMV_TRY(expr)                              \
+  do {                                               \
+    hipError_t e_ = (expr);                          \
+    if (e_ != hipSuccess) return status_from_hip(e_); \
+  } while (0)
+
+// Radix schedule for the length-L complex FFT, L = 2^a 5^b. Radix 8 while
+// more than four factors of two remain, then 4 4 / 8 / 4 / 2, then the 5s.
+bool build_geometry(int64_t L, FftGeom *g) {
+  int64_t r = L;
+  int a = 0, b = 0;
+  while (r % 2 == 0) r /= 2, ++a;
+  while (r % 5 == 0) r /= 5, ++b;
+  if (r != 1) return false;
+  int np = 0;
+  auto push = [&](int R) {
+    if (np >= kMaxPasses) return false;
+    g->radix[np++] = R;
+    return true;
+  };
+  while (a > 4) {
+    if (!push(8)) return false;
+    a -= 3;
+  }
+  if (a == 4) {
+    if (!push(4) || !push(4)) return false;
+  } else if (a == 3) {
+    if (!push(8)) return false;
+  } else if (a == 2) {
+    if (!push(4)) return false;
+  } else if (a == 1) {
+    if (!push(2)) return false;
+  }
+  for (int i = 0; i < b; ++i)
+    if (!push(5)) return false;
+  g->L = static_cast<int>(L);
+  g->npass = np;
+  int ns = 1;
+  for (int p = 0; p < np; ++p) {
+    g->ns[p] = ns;
+    g->twstep[p] = static_cast<int>((2 * L) / (static_cast<int64_t>(ns) * g->radix[p]));
+    ns *= g->radix[p];
+  }
+  return true;
+}
+
+// exp(-2 pi i t / N) with the angle reduced exactly in integers to
+// [0, pi/4] by the symmetries of sine and cosine, so that multiples of pi/4
+// come out exact (or correctly rounded) and the table is symmetric.
+void unit_root(int64_t t, int64_t N, double *re, double *im) {
+  int64_t u = 4 * (t % N);  // angle = 2 pi u / (4N)
+  const int64_t full = 4 * N;
+  double ss = 1.0, sc = 1.0;
+  if (u > full / 2) {  // 2 pi - a
+    u = full - u;
+    ss = -1.0;
+  }
+  if (u > N) {  // pi - a
+    u = 2 * N - u;
+    sc = -1.0;
+  }
+  bool swap = false;
+  if (2 * u > N) {  // pi/2 - a
+    u = N - u;
+    swap = true;
+  }
+  const double a = (M_PI / 2.0) * static_cast<double>(u) / static_cast<double>(N);
+  double c = std::cos(a), s = std::sin(a);
+  if (u == 0) c = 1.0, s = 0.0;
+  if (swap) std::swap(c, s);
+  *re = sc * c;
+  *im = -(ss * s);
+}
+
+void release(fftmv_plan_s *p) {
+  for (int i = 0; i < p->nalloc; ++i) (void)hipFree(p->allocs[i]);
+  p->nalloc = 0;
+}
+
+hipError_t dev_alloc(fftmv_plan_s *p, void **ptr, size_t bytes) {
+  if (p->nalloc >= 16) return hipErrorUnknown;
+  void *q = nullptr;
+  hipError_t e = hipMalloc(&q, bytes ? bytes : 16);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return e;
+  }
+  p->allocs[p->nalloc++] = q;
+  *ptr = q;
+  return hipSuccess;
+}
+
+bool aligned8(const void *q) { return (reinterpret_cast<uintptr_t>(q) & 7u) == 0; }
+
+// stage-boundary buffer precisions: the narrower of the two stages
+bool buf_f32(uint32_t prec, int dir, int s) { return fp32(prec, dir, s) || fp32(prec, dir, s + 1); }
+
+int64_t channels_in(const fftmv_plan_s *p, int dir) { return dir == 0 ? p->Nm : p->Nd; }
+int64_t channels_out(const fftmv_plan_s *p, int dir) { return dir == 0 ? p->Nd : p->Nm; }
+
+bool needs_fhat32(uint32_t prec) { return fp32(prec, 0, 3) || fp32(prec, 1, 3); }
+bool needs_fhat64(uint32_t prec) { return !fp32(prec, 0, 3) || !fp32(prec, 1, 3); }
+
+const void *twiddles(const fftmv_plan_s *p, bool f32) { return f32 ? p->tw32 : p->tw64; }
+
+// ------------------------------------------------------------- stages
+// Stage 1 alone: m (FP64) -> buf 1 (the live half of the padded input).
+hipError_t stage_pad(const fftmv_plan_s *p, int dir, const double *in, hipStream_t s) {
+  CastArgs a;
+  a.rows = p->Nt;
+  a.cols = channels_in(p, dir);
+  a.src = in;
+  a.lds = a.cols;
+  a.src_f32 = false;
+  a.dst = p->buf[dir][1].p;
+  a.ldd = p->buf[dir][1].ld;
+  a.dst_f32 = buf_f32(p->prec, dir, 1);
+  return launch_cast(a, s);
+}
+
+// Stage 2: forward FFT of the input channels into buf 2. With from_user the
+// stage-1 pad is folded into the load (reads the FP64 input directly and
+// rounds it when stage 1 or 2 is FP32).
+hipError_t stage_fft(const fftmv_plan_s *p, int dir, const double *user_in, bool from_user, hipStream_t s) {
+  const bool cf32 = fp32(p->prec, dir, 2);
+  FwdFftArgs a;
+  a.Nt = p->Nt;
+  a.nchan = channels_in(p, dir);
+  if (from_user) {
+    a.src = user_in;
+    a.src_ld = a.nchan;
+    a.src_f32 = false;
+    a.round_f32 = fp32(p->prec, dir, 1);
+  } else {
+    a.src = p->buf[dir][1].p;
+    a.src_ld = p->buf[dir][1].ld;
+    a.src_f32 = buf_f32(p->prec, dir, 1);
+    a.round_f32 = false;
+  }
+  const StageBuf &o = p->buf[dir][2];
+  if (buf_f32(p->prec, dir, 2)) {
+    a.dst32 = o.p;
+    a.fstride32 = o.ld;
+    a.ldr32 = 0;
+  } else {
+    a.dst64 = o.p;
+    a.fstride64 = o.ld;
+    a.ldr64 = 0;
+  }
+  a.cpr = a.nchan;
+  return launch_fft_forward(p->geom, a, cf32, twiddles(p, cf32), s);
+}
+
+// Stage 3: per-frequency GEMV (F) or conjugate-transpose GEMV (F*).
+hipError_t stage_sbgemv(const fftmv_plan_s *p, int dir, hipStream_t s) {
+  const bool cf32 = fp32(p->prec, dir, 3);
+  SbgemvArgs a;
+  a.K = p->K;
+  a.Nd = p->Nd;
+  a.Nm = p->Nm;
+  a.F = cf32 ? p->fhat32 : p->fhat64;
+  a.ldF = cf32 ? p->ldF32 : p->ldF64;
+  a.x = p->buf[dir][2].p;
+  a.ldx = p->buf[dir][2].ld;
+  a.x_f32 = buf_f32(p->prec, dir, 2);
+  a.y = p->buf[dir][3].p;
+  a.ldy = p->buf[dir][3].ld;
+  a.y_f32 = buf_f32(p->prec, dir, 3);
+  if (!a.F) return hipErrorInvalidValue;
+  return dir == 0 ? launch_sbgemv_n(a, cf32, s) : launch_sbgemv_c(a, cf32, s);
+}
+
+// Stage 4: inverse FFT of the output channels. With to_user the stage-5
+// unpad is folded into the store (writes FP64, rounded when stage 5 is FP32).
+hipError_t stage_ifft(const fftmv_plan_s *p, int dir, double *user_out, bool to_user, hipStream_t s) {
+  const bool cf32 = fp32(p->prec, dir, 4);
+  InvFftArgs a;
+  a.Nt = p->Nt;
+  a.nchan = channels_out(p, dir);
+  a.src = p->buf[dir][3].p;
+  a.src_ld = p->buf[dir][3].ld;
+  a.src_f32 = buf_f32(p->prec, dir, 3);
+  if (to_user) {
+    a.dst = user_out;
+    a.dst_ld = a.nchan;
+    a.dst_f32 = false;
+    a.round_f32 = fp32(p->prec, dir, 5);
+  } else {
+    a.dst = p->buf[dir][4].p;
+    a.dst_ld = p->buf[dir][4].ld;
+    a.dst_f32 = buf_f32(p->prec, dir, 4);
+    a.round_f32 = false;
+  }
+  return launch_fft_inverse(p->geom, a, cf32, twiddles(p, cf32), s);
+}
+
+// Stage 5 alone: buf 4 -> FP64 output.
+hipError_t stage_unpad(const fftmv_plan_s *p, int dir, double *out, hipStream_t s) {
+  CastArgs a;
+  a.rows = p->Nt;
+  a.cols = channels_out(p, dir);
+  a.src = p->buf[dir][4].p;
+  a.lds = p->buf[dir][4].ld;
+  a.src_f32 = buf_f32(p->prec, dir, 4);
+  a.dst = out;
+  a.ldd = a.cols;
+  a.dst_f32 = false;
+  return launch_cast(a, s);
+}
+
+hipError_t run_range(const fftmv_plan_s *p, int dir, int first, int last, const double *in, double *out,
+                     hipStream_t s) {
+  hipError_t e = hipSuccess;
+  for (int st = first; st <= last && e == hipSuccess; ++st) {
+    switch (st) {
+      case 1: e = stage_pad(p, dir, in, s); break;
+      case 2: e = stage_fft(p, dir, nullptr, false, s); break;
+      case 3: e = stage_sbgemv(p, dir, s); break;
+      case 4: e = stage_ifft(p, dir, nullptr, false, s); break;
+      default: e = stage_unpad(p, dir, out, s); break;
+    }
+  }
+  return e;
+}
+
+int apply_dir(fftmv_plan_t p, int dir, const double *in, double *out, hipStream_t s) {
+  if (!p || !in || !out || !aligned8(in) || !aligned8(out)) return FFTMV_ERR_INVALID_ARG;
+  if (static_cast<const void *>(in) == static_cast<const void *>(out)) return FFTMV_ERR_INVALID_ARG;
+  try {
+    hipError_t e;
+    if (p->flags & FFTMV_FLAG_STAGED) {
+      e = run_range(p, dir, 1, 5, in, out, s);
+    } else {
+      e = stage_fft(p, dir, in, true, s);
+      if (e == hipSuccess) e = stage_sbgemv(p, dir, s);
+      if (e == hipSuccess) e = stage_ifft(p, dir, out, true, s);
+    }
+    return status_from_hip(e);
+  } catch (...) {
+    return FFTMV_ERR_INTERNAL;
+  }
+}
+
+int setup_impl(fftmv_plan_s *p, const double *F, hipStream_t s) {
+  const int64_t Nm = p->Nm, Nd = p->Nd, Nt = p->Nt, K = p->K;
+  const bool want32 = needs_fhat32(p->prec) || (p->flags & FFTMV_FLAG_FHAT_BOTH);
+  const bool want64 = needs_fhat64(p->prec) || (p->flags & FFTMV_FLAG_FHAT_BOTH);
+
+  // Fhat
+  int64_t n32 = 0, n64 = 0, tmp = 0;
+  p->ldF32 = padded_ld(Nm);
+  p->ldF64 = Nm;
+  if (!mul_ok(K, Nd, &tmp) || !mul_ok(tmp, p->ldF32, &n32) || !mul_ok(tmp, p->ldF64, &n64) ||
+      !mul_ok(n64, 16, &tmp))
+    return FFTMV_ERR_OUT_OF_MEMORY;
+  if (want32) {
+    FFTMV_TRY(dev_alloc(p, &p->fhat32, static_cast<size_t>(n32) * 8));
+    FFTMV_TRY(hipMemsetAsync(p->fhat32, 0, static_cast<size_t>(n32) * 8, s));
+    p->fhat_bytes += static_cast<size_t>(n32) * 8;
+  }
+  if (want64) {
+    FFTMV_TRY(dev_alloc(p, &p->fhat64, static_cast<size_t>(n64) * 16));
+    p->fhat_bytes += static_cast<size_t>(n64) * 16;
+  }
+
+  // twiddles: w_N^t for t < N = 2 Nt, in both precisions
+  const int64_t N = 2 * Nt;
+  {
+    double *h64 = new (std::nothrow) double[2 * N];
+    float *h32 = new (std::nothrow) float[2 * N];
+    if (!h64 || !h32) {
+      delete[] h64;
+      delete[] h32;
+      return FFTMV_ERR_INTERNAL;
+    }
+    for (int64_t t = 0; t < N; ++t) {
+      unit_root(t, N, &h64[2 * t], &h64[2 * t + 1]);
+      h32[2 * t] = static_cast<float>(h64[2 * t]);
+      h32[2 * t + 1] = static_cast<float>(h64[2 * t + 1]);
+    }
+    hipError_t e = dev_alloc(p, &p->tw64, static_cast<size_t>(N) * 16);
+    if (e == hipSuccess) e = dev_alloc(p, &p->tw32, static_cast<size_t>(N) * 8);
+    if (e == hipSuccess) e = hipMemcpy(p->tw64, h64, static_cast<size_t>(N) * 16, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(p->tw32, h32, static_cast<size_t>(N) * 8, hipMemcpyHostToDevice);
+    delete[] h64;
+    delete[] h32;
+    FFTMV_TRY(e);
+    p->ws_bytes += static_cast<size_t>(N) * 24;
+  }
+
+  // stage buffers, sized for FP64 so that any precision mask fits
+  for (int dir = 0; dir < 2; ++dir) {
+    const int64_t ldi = padded_ld(channels_in(p, dir)), ldo = padded_ld(channels_out(p, dir));
+    const int64_t rows[5] = {0, Nt, K, K, Nt};
+    const int64_t lds[5] = {0, ldi, ldi, ldo, ldo};
+    const int64_t esz[5] = {0, 8, 16, 16, 8};
+    for (int st = 1; st <= 4; ++st) {
+      int64_t n = 0, bytes = 0;
+      if (!mul_ok(rows[st], lds[st], &n) || !mul_ok(n, esz[st], &bytes)) return FFTMV_ERR_OUT_OF_MEMORY;
+      FFTMV_TRY(dev_alloc(p, &p->buf[dir][st].p, static_cast<size_t>(bytes)));
+      FFTMV_TRY(hipMemsetAsync(p->buf[dir][st].p, 0, static_cast<size_t>(bytes), s));
+      p->buf[dir][st].ld = lds[st];
+      p->ws_bytes += static_cast<size_t>(bytes);
+    }
+  }
+
+  // Fhat_k = DFT of every zero-padded (r, c) series, computed in FP64 and
+  // rounded once to each stored precision
+  FwdFftArgs a;
+  a.Nt = Nt;
+  a.nchan = Nd * Nm;
+  a.src = F;
+  a.src_ld = Nd * Nm;
+  a.src_f32 = false;
+  a.round_f32 = false;
+  a.dst32 = p->fhat32;
+  a.fstride32 = Nd * p->ldF32;
+  a.ldr32 = p->ldF32;
+  a.dst64 = p->fhat64;
+  a.fstride64 = Nd * p->ldF64;
+  a.ldr64 = p->ldF64;
+  a.cpr = Nm;
+  FFTMV_TRY(launch_fft_forward(p->geom, a, false, p->tw64, s));
+  FFTMV_TRY(hipStreamSynchronize(s));
+  return FFTMV_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fftmv_setup(fftmv_plan_t *out, const double *F_dev, int64_t Nm, int64_t Nd, int64_t Nt, uint32_t mask,
+                hipStream_t stream) {
+  if (!out || !F_dev || !aligned8(F_dev) || Nm < 1 || Nd < 1 || Nt < 1) return FFTMV_ERR_INVALID_ARG;
+  if (mask & ~(FFTMV_PREC_BITS | FFTMV_FLAG_BITS)) return FFTMV_ERR_INVALID_ARG;
+  if (Nm > INT32_MAX || Nd > INT32_MAX) return FFTMV_ERR_UNSUPPORTED_SIZE;
+  if (Nt > 4096) return FFTMV_ERR_UNSUPPORTED_SIZE;
+  try {
+    fftmv_plan_s *p = new (std::nothrow) fftmv_plan_s();
+    if (!p) return FFTMV_ERR_INTERNAL;
+    p->Nm = Nm;
+    p->Nd = Nd;
+    p->Nt = Nt;
+    p->K = Nt + 1;
+    p->prec = mask & FFTMV_PREC_BITS;
+    p->flags = mask & FFTMV_FLAG_BITS;
+    if (!build_geometry(Nt, &p->geom) || fft_channels_per_block(p->geom, false, 1) == 0 ||
+        fft_channels_per_block(p->geom, true, 1) == 0) {
+      delete p;
+      return FFTMV_ERR_UNSUPPORTED_SIZE;
+    }
+    if (hipGetDevice(&p->device) != hipSuccess) {
+      delete p;
+      return FFTMV_ERR_HIP;
+    }
+    int st = setup_impl(p, F_dev, stream);
+    if (st != FFTMV_SUCCESS) {
+      (void)hipStreamSynchronize(stream);
+      release(p);
+      delete p;
+      return st;
+    }
+    *out = p;
+    return FFTMV_SUCCESS;
+  } catch (...) {
+    return FFTMV_ERR_INTERNAL;
+  }
+}
+
+int fftmv_apply(fftmv_plan_t plan, const double *m_dev, double *v_dev, hipStream_t stream) {
+  return apply_dir(plan, FFTMV_DIR_F, m_dev, v_dev, stream);
+}
+
+int fftmv_apply_adjoint(fftmv_plan_t plan, const double *d_dev, double *w_dev, hipStream_t stream) {
+  return apply_dir(plan, FFTMV_DIR_FADJ, d_dev, w_dev, stream);
+}
+
+int fftmv_destroy(fftmv_plan_t plan) {
+  if (!plan) return FFTMV_SUCCESS;
+  int cur = 0;
+  bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  (void)hipSetDevice(plan->device);
+  hipError_t e = hipDeviceSynchronize();
+  release(plan);
+  if (have_cur) (void)hipSetDevice(cur);
+  delete plan;
+  return status_from_hip(e);
+}
+
+const char *fftmv_status_string(int status) {
+  switch (status) {
+    case FFTMV_SUCCESS: return "success";
+    case FFTMV_ERR_INVALID_ARG: return "invalid argument";
+    case FFTMV_ERR_UNSUPPORTED_SIZE: return "unsupported size (2*Nt must be 2^a*5^b with Nt <= 4096)";
+    case FFTMV_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case FFTMV_ERR_HIP: return "HIP runtime error";
+    case FFTMV_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+int fftmv_query(fftmv_plan_t plan, size_t *fhat_bytes, size_t *workspace_bytes) {
+  if (!plan) return FFTMV_ERR_INVALID_ARG;
+  if (fhat_bytes) *fhat_bytes = plan->fhat_bytes;
+  if (workspace_bytes) *workspace_bytes = plan->ws_bytes;
+  return FFTMV_SUCCESS;
+}
+
+int fftmv_set_mask(fftmv_plan_t plan, uint32_t prec_mask) {
+  if (!plan || (prec_mask & ~FFTMV_PREC_BITS)) return FFTMV_ERR_INVALID_ARG;
+  if ((needs_fhat32(prec_mask) && !plan->fhat32) || (needs_fhat64(prec_mask) && !plan->fhat64))
+    return FFTMV_ERR_INVALID_ARG;
+  // Buffers change element type with the mask: clear them so that padding
+  // entries read by the 16-byte vector loads hold zeros in the new layout.
+  for (int dir = 0; dir < 2; ++dir)
+    for (int st = 1; st <= 4; ++st) {
+      const int64_t rows = (st == 1 || st == 4) ? plan->Nt : plan->K;
+      const size_t bytes = static_cast<size_t>(rows * plan->buf[dir][st].ld) * ((st == 1 || st == 4) ? 8 : 16);
+      if (hipMemset(plan->buf[dir][st].p, 0, bytes) != hipSuccess) return FFTMV_ERR_HIP;
+    }
+  if (hipDeviceSynchronize() != hipSuccess) return FFTMV_ERR_HIP;
+  plan->prec = prec_mask;
+  return FFTMV_SUCCESS;
+}
+
+int fftmv_run_stages(fftmv_plan_t plan, int dir, int first, int last, const double *in, double *out,
+                     hipStream_t stream) {
+  if (!plan || (dir != 0 && dir != 1) || first < 1 || last > 5 || first > last) return FFTMV_ERR_INVALID_ARG;
+  if (first == 1 && (!in || !aligned8(in))) return FFTMV_ERR_INVALID_ARG;
+  if (last == 5 && (!out || !aligned8(out))) return FFTMV_ERR_INVALID_ARG;
+  try {
+    return status_from_hip(run_range(plan, dir, first, last, in, out, stream));
+  } catch (...) {
+    return FFTMV_ERR_INTERNAL;
+  }
+}
+
+int fftmv_buffer(fftmv_plan_t plan, int which, void **ptr, int64_t *ld, int *elem_bytes) {
+  if (!plan) return FFTMV_ERR_INVALID_ARG;
+  void *q = nullptr;
+  int64_t l = 0;
+  int eb = 0;
+  if (which == 0) {
+    q = plan->fhat32, l = plan->ldF32, eb = 8;
+  } else if (which == 1) {
+    q = plan->fhat64, l = plan->ldF64, eb = 16;
+  } else {
+    const int dir = (which - 10) / 10, st = (which - 10) % 10;
+    if (which < 10 || dir > 1 || st < 1 || st > 4) return FFTMV_ERR_INVALID_ARG;
+    q = plan->buf[dir][st].p;
+    l = plan->buf[dir][st].ld;
+    const bool f32 = buf_f32(plan->prec, dir, st);
+    eb = (st == 1 || st == 4) ? (f32 ? 4 : 8) : (f32 ? 8 : 16);
+  }
+  if (ptr) *ptr = q;
+  if (ld) *ld = l;
+  if (elem_bytes) *elem_bytes = eb;
+  return FFTMV_SUCCESS;
+}
+
+int fftmv_version(void) { return kVersion; }
+
+}  // extern "C"

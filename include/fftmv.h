@@ -1,0 +1,165 @@
+/*
+ * fftmv -- block lower-triangular Toeplitz matvec through the FFT, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operation ("Mixed-precision FFTMatvec performance optimization on AMD
+ * GPUs", sections 1 and 1.1): F is an Nt x Nt grid of blocks, block (i, j)
+ * being the Nd x Nm matrix F_{i-j} for i >= j and zero above the diagonal.
+ *
+ *     v = F m      v_i = sum_{j <= i}     F_{i-j}   m_j     (i < Nt)
+ *     w = F* d     w_j = sum_{i >= j}     F_{i-j}^T d_i     (j < Nt)
+ *
+ * Both run in the page's five stages: (1) broadcast + zero pad each channel
+ * to length N = 2 Nt, (2) batched real FFT, (3) one complex GEMV per
+ * frequency k = 0..Nt against the precomputed frequency blocks
+ * Fhat_k = sum_n F_n exp(-2 pi i n k / N) -- the conjugate transpose
+ * Fhat_k^H for F* (section 1.2) -- (4) batched inverse real FFT, (5) unpad
+ * (keep time steps 0..Nt-1) and reduce. On one GPU the broadcast and the
+ * reduce are the identity.
+ *
+ * Mixed precision (section 2.2): each of the five stages of each direction
+ * runs in FP32 or FP64, chosen by a 10-bit mask. The page's configurations
+ * for a 1e-7 error budget are FFTMV_MIXED_F (FFT + SBGEMV in FP32) and
+ * FFTMV_MIXED_FADJ (SBGEMV + inverse FFT in FP32).
+ *
+ * Layouts (row-major, all device memory, FP64 at the interface):
+ *   F    [Nt][Nd][Nm]   block F_k starts at F + k*Nd*Nm
+ *   m, w [Nt][Nm]       time step j is the contiguous Nm-vector m + j*Nm
+ *   d, v [Nt][Nd]
+ * Pointers need 8-byte alignment (natural for double).
+ *
+ * Supported sizes: 1 <= Nm, Nd <= 2^31 - 1; 1 <= Nt <= 4096 with
+ * 2 Nt = 2^a 5^b; any other size returns FFTMV_ERR_UNSUPPORTED_SIZE.
+ *
+ * Ownership and concurrency:
+ *   - fftmv_setup is synchronous: when it returns the frequency blocks are
+ *     built and the caller may free F. The plan owns Fhat, its twiddle
+ *     tables and one workspace, all in device memory.
+ *   - fftmv_apply / fftmv_apply_adjoint are asynchronous on the stream they
+ *     are given; they allocate nothing and never synchronise. The caller owns
+ *     the vectors and the streams. Outputs must not alias inputs.
+ *   - Applies on one plan share its workspace: they must be ordered (one
+ *     stream, or caller synchronisation). Different plans are independent.
+ *
+ * Errors: every entry point returns FFTMV_SUCCESS (0) or a negative status.
+ * Arguments are checked before any device work; no C++ exception crosses
+ * this interface. A fault inside a kernel surfaces at the caller's next
+ * synchronisation of the stream, as usual in HIP. NaN and Inf inputs are
+ * not masked: they propagate (the FFT spreads them over their channel).
+ */
+#ifndef FFTMV_H
+#define FFTMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef FFTMV_API
+#define FFTMV_API __attribute__((visibility("default")))
+#endif
+
+/* ----------------------------------------------------------------- status */
+#define FFTMV_SUCCESS 0
+#define FFTMV_ERR_INVALID_ARG (-1)      /* null pointer, bad size/mask/stage  */
+#define FFTMV_ERR_UNSUPPORTED_SIZE (-2) /* 2 Nt not 2^a 5^b, or Nt too large  */
+#define FFTMV_ERR_OUT_OF_MEMORY (-3)    /* device allocation failed           */
+#define FFTMV_ERR_HIP (-4)              /* a HIP runtime call or launch failed */
+#define FFTMV_ERR_INTERNAL (-5)         /* unexpected library condition       */
+
+/* ------------------------------------------------------- precision mask
+ * Bit (5*dir + stage - 1) set = that stage runs in FP32, clear = FP64.
+ * dir 0 is F, dir 1 is F*; stages are numbered in pipeline order:
+ * 1 pad, 2 forward FFT, 3 SBGEMV, 4 inverse FFT, 5 unpad. */
+#define FFTMV_DIR_F 0
+#define FFTMV_DIR_FADJ 1
+#define FFTMV_FP32(dir, stage) (1u << (5u * (unsigned)(dir) + (unsigned)(stage) - 1u))
+#define FFTMV_ALL_FP64 0x000u
+#define FFTMV_MIXED_F 0x006u    /* F:  stages 2 (FFT) and 3 (SBGEMV) in FP32  */
+#define FFTMV_MIXED_FADJ 0x180u /* F*: stages 3 (SBGEMV) and 4 (IFFT) in FP32 */
+#define FFTMV_MIXED 0x186u      /* both of the above                          */
+#define FFTMV_PREC_BITS 0x3FFu
+
+/* ------------------------------------------------------------ plan flags
+ * OR-ed into the mask argument of fftmv_setup (bits above the precision). */
+/* Run the five stages as five kernels with materialised pad and unpad
+ * buffers, instead of folding pad into the forward FFT's load and unpad into
+ * the inverse FFT's store (same numbers, more memory traffic). */
+#define FFTMV_FLAG_STAGED (1u << 16)
+/* Keep Fhat in both complex64 and complex128 so that fftmv_set_mask can
+ * switch to any precision mask without a new setup. */
+#define FFTMV_FLAG_FHAT_BOTH (1u << 17)
+#define FFTMV_FLAG_BITS (FFTMV_FLAG_STAGED | FFTMV_FLAG_FHAT_BOTH)
+
+typedef struct fftmv_plan_s *fftmv_plan_t;
+
+/* Build a plan: validate, allocate Fhat (complex64 if some SBGEMV stage is
+ * FP32, complex128 if some SBGEMV stage is FP64; both with
+ * FFTMV_FLAG_FHAT_BOTH), the twiddle tables and the workspace, then compute
+ * Fhat_k for k = 0..Nt in FP64 on the device (batched real FFT of the Nd*Nm
+ * zero-padded series of F) and round it once to each stored precision.
+ * Returns after the stream has been synchronised.
+ *   out     receives the plan; untouched on failure (nothing leaks)
+ *   F_dev   device pointer, [Nt][Nd][Nm] FP64, read only, not retained
+ *   mask    precision bits (FFTMV_PREC_BITS) | flags (FFTMV_FLAG_BITS)
+ *   stream  stream for the setup work (0 = null stream) */
+FFTMV_API int fftmv_setup(fftmv_plan_t *out, const double *F_dev, int64_t Nm, int64_t Nd, int64_t Nt,
+                uint32_t mask, hipStream_t stream);
+
+/* v = F m (section 1.1). m_dev [Nt][Nm] FP64 in, v_dev [Nt][Nd] FP64 out,
+ * both device pointers; runs asynchronously on stream. */
+FFTMV_API int fftmv_apply(fftmv_plan_t plan, const double *m_dev, double *v_dev, hipStream_t stream);
+
+/* w = F* d with the conjugate-transpose frequency product (section 1.2).
+ * d_dev [Nt][Nd] FP64 in, w_dev [Nt][Nm] FP64 out; asynchronous. */
+FFTMV_API int fftmv_apply_adjoint(fftmv_plan_t plan, const double *d_dev, double *w_dev, hipStream_t stream);
+
+/* Free the plan's device memory. Synchronises the device first so that no
+ * queued apply still uses it. NULL is accepted. */
+FFTMV_API int fftmv_destroy(fftmv_plan_t plan);
+
+/* Static string for a status code; never NULL. */
+FFTMV_API const char *fftmv_status_string(int status);
+
+/* Device bytes held by the plan: Fhat (all stored precisions) and the
+ * workspace (stage buffers + twiddles). Either pointer may be NULL. */
+FFTMV_API int fftmv_query(fftmv_plan_t plan, size_t *fhat_bytes, size_t *workspace_bytes);
+
+/* Change the precision bits of a plan (flags are kept). Fails with
+ * FFTMV_ERR_INVALID_ARG if the new mask needs an Fhat precision the plan did
+ * not store. Must be ordered with the plan's applies like any other call on
+ * the plan. */
+FFTMV_API int fftmv_set_mask(fftmv_plan_t plan, uint32_t prec_mask);
+
+/* Run stages first..last (1..5) of one direction, for stage-by-stage
+ * checking. Stage s reads the buffer stage s-1 wrote (for s = 1, the FP64
+ * input `in`) and writes its own buffer (for s = 5, the FP64 output `out`);
+ * buffers are those of fftmv_buffer. Always runs the five-kernel form.
+ * in/out may be NULL when first > 1 / last < 5. Asynchronous. */
+FFTMV_API int fftmv_run_stages(fftmv_plan_t plan, int dir, int first, int last, const double *in, double *out,
+                     hipStream_t stream);
+
+/* Describe a plan-owned device buffer:
+ *   which = 0: Fhat complex64, 1: Fhat complex128 -- [Nt+1][Nd][ld]
+ *   which = 10 + 10*dir + s (s = 1..4): output buffer of stage s of
+ *     direction dir -- stage 1: [Nt][ld] real (the nonzero half of the
+ *     padded input; the zero half is never stored), stage 2 and 3:
+ *     [Nt+1][ld] complex, stage 4: [Nt][ld] real.
+ * ptr: device pointer (NULL if not allocated); ld: leading dimension in
+ * elements; elem_bytes: 4/8 (real FP32/FP64) or 8/16 (complex64/128) --
+ * buffers between two stages are stored in the narrower of the two stages'
+ * precisions. Any out pointer may be NULL. */
+FFTMV_API int fftmv_buffer(fftmv_plan_t plan, int which, void **ptr, int64_t *ld, int *elem_bytes);
+
+/* Library version, (major << 16) | (minor << 8) | patch. */
+FFTMV_API int fftmv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFTMV_H */
