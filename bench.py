@@ -31,8 +31,8 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--shape", default="main", choices=["tiny", "small", "main", "scale"])
     ap.add_argument("--mask", type=lambda s: int(s, 0), default=0x186)
     ap.add_argument("--staged", action="store_true", help="five-kernel form (pad/unpad materialised)")

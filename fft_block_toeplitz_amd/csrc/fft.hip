@@ -19,25 +19,22 @@
 // stride-1 across lanes. The length-L complex FFT is a Stockham autosort
 // (self-sorting, no bit reversal) with radix 2/4/5/8 passes; each pass reads
 // all its butterfly inputs into registers, synchronises, then writes in
-// place.
+// place. The first pass takes its inputs straight from global memory (all
+// of a thread's loads in flight at once) and, in the inverse, the last pass
+// stores straight to global memory, so the data cross LDS only between
+// passes. Channel tiles are numbered XCD-contiguously so that neighbouring
+// tiles, which share cache lines, share an L2.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace fftmv {
 namespace {
 
-// Butterflies a thread keeps in registers in one pass (bounded register
-// use); the host picks C so that every pass fits.
-template <typename T, int R>
-constexpr int butterflies_per_thread() {
-  if (sizeof(T) == 4) return R == 2 ? 16 : R == 4 ? 8 : R == 5 ? 7 : 4;
-  return R == 2 ? 8 : R == 4 ? 4 : R == 5 ? 4 : 2;
-}
-
-int host_butterflies_per_thread(bool f32, int R) {
-  if (f32) return R == 2 ? 16 : R == 4 ? 8 : R == 5 ? 7 : 4;
-  return R == 2 ? 8 : R == 4 ? 4 : R == 5 ? 4 : 2;
-}
+// A thread keeps at most VMAX complex values in registers during a pass,
+// i.e. VMAX / R butterflies of radix R; the host picks C (channels per
+// workgroup) and VMAX so that every pass of the schedule fits.
+constexpr int kVmaxSmall = 20;
+constexpr int kVmaxLarge = 40;
 
 // ---------------------------------------------------------------- DFTs
 // y_q = sum_p x_p exp(S 2 pi i p q / R), in place, S = -1 forward, +1 inverse.
@@ -109,13 +106,22 @@ __device__ __forceinline__ void dft(cx<T> *x) {
   else dft8<S>(x);
 }
 
+template <typename T, int R, int S>
+__device__ __forceinline__ void twiddle(cx<T> *v, int k, int twstep, const cx<T> *__restrict__ tw) {
+#pragma unroll
+  for (int q = 1; q < R; ++q) {
+    cx<T> w = tw[k * q * twstep];
+    v[q] = S < 0 ? cmul(v[q], w) : cmulc(v[q], w);
+  }
+}
+
 // One Stockham pass of radix R over the [L][C] LDS tile. Butterfly j of
 // channel c reads elements j + q L/R, multiplies input q by
 // w_{Ns R}^{(j mod Ns) q} and writes output q to (j - j mod Ns) R + j mod Ns + q Ns.
-template <typename T, int R, int S>
-__device__ __forceinline__ void stockham_pass(cx<T> *lds, int L, int logC, int Ns, int twstep,
-                                              const cx<T> *__restrict__ tw) {
-  constexpr int B = butterflies_per_thread<T, R>();
+template <typename T, int R, int S, int VMAX>
+__device__ __forceinline__ void lds_pass(cx<T> *lds, int L, int logC, int Ns, int twstep,
+                                         const cx<T> *__restrict__ tw) {
+  constexpr int B = VMAX / R;
   const int C = 1 << logC;
   const int Lr = L / R;
   const int nb = Lr << logC;
@@ -136,13 +142,7 @@ __device__ __forceinline__ void stockham_pass(cx<T> *lds, int L, int logC, int N
     if (b < nb) {
       int c = b & (C - 1), j = b >> logC;
       int k = j % Ns;
-      if (Ns > 1) {
-#pragma unroll
-        for (int q = 1; q < R; ++q) {
-          cx<T> w = tw[k * q * twstep];
-          v[i][q] = S < 0 ? cmul(v[i][q], w) : cmulc(v[i][q], w);
-        }
-      }
+      if (Ns > 1) twiddle<T, R, S>(v[i], k, twstep, tw);
       dft<R, S>(v[i]);
       int base = (j - k) * R + k;
 #pragma unroll
@@ -152,49 +152,158 @@ __device__ __forceinline__ void stockham_pass(cx<T> *lds, int L, int logC, int N
   __syncthreads();
 }
 
-template <typename T, int S>
-__device__ __forceinline__ void all_passes(cx<T> *lds, const FftGeom &g, int logC, const cx<T> *__restrict__ tw) {
-  for (int p = 0; p < g.npass; ++p) {
-    switch (g.radix[p]) {
-      case 2: stockham_pass<T, 2, S>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
-      case 4: stockham_pass<T, 4, S>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
-      case 5: stockham_pass<T, 5, S>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
-      default: stockham_pass<T, 8, S>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+// First pass (Ns = 1, no twiddles): input n of this thread's channel comes
+// from get(n), output n goes to put(n, value). All loads of the thread are
+// issued before any butterfly.
+template <typename T, int R, int S, int VMAX, typename Get, typename Put>
+__device__ __forceinline__ void first_pass(int L, int logC, Get get, Put put) {
+  constexpr int B = VMAX / R;
+  const int Lr = L / R;
+  const int nb = Lr << logC;
+  cx<T> v[B][R];
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    int b = threadIdx.x + i * kBlock;
+    if (b < nb) {
+      int j = b >> logC;
+#pragma unroll
+      for (int q = 0; q < R; ++q) v[i][q] = get(j + q * Lr);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    int b = threadIdx.x + i * kBlock;
+    if (b < nb) {
+      int j = b >> logC;
+      dft<R, S>(v[i]);
+#pragma unroll
+      for (int q = 0; q < R; ++q) put(j * R + q, v[i][q]);
     }
   }
 }
 
+// Last pass (Ns = L/R) reading the LDS tile and handing output n to put.
+template <typename T, int R, int S, int VMAX, typename Put>
+__device__ __forceinline__ void last_pass(const cx<T> *lds, int L, int logC, int twstep,
+                                          const cx<T> *__restrict__ tw, Put put) {
+  constexpr int B = VMAX / R;
+  const int C = 1 << logC;
+  const int Lr = L / R;  // == Ns of this pass
+  const int nb = Lr << logC;
+  cx<T> v[B][R];
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    int b = threadIdx.x + i * kBlock;
+    if (b < nb) {
+      int c = b & (C - 1), j = b >> logC;
+#pragma unroll
+      for (int q = 0; q < R; ++q) v[i][q] = lds[((j + q * Lr) << logC) + c];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    int b = threadIdx.x + i * kBlock;
+    if (b < nb) {
+      int j = b >> logC;
+      if (Lr > 1) twiddle<T, R, S>(v[i], j, twstep, tw);
+      dft<R, S>(v[i]);
+#pragma unroll
+      for (int q = 0; q < R; ++q) put(j + q * Lr, v[i][q]);
+    }
+  }
+}
+
+template <typename T, int S, int VMAX>
+__device__ __forceinline__ void middle_passes(cx<T> *lds, const FftGeom &g, int first, int last, int logC,
+                                              const cx<T> *__restrict__ tw) {
+  for (int p = first; p < last; ++p) {
+    switch (g.radix[p]) {
+      case 2: lds_pass<T, 2, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+      case 4: lds_pass<T, 4, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+      case 5: lds_pass<T, 5, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+      default: lds_pass<T, 8, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+    }
+  }
+}
+
+template <typename T, int S, int VMAX, typename Get, typename Put>
+__device__ __forceinline__ void first_pass_any(int R, int L, int logC, Get get, Put put) {
+  switch (R) {
+    case 2: first_pass<T, 2, S, VMAX>(L, logC, get, put); break;
+    case 4: first_pass<T, 4, S, VMAX>(L, logC, get, put); break;
+    case 5: first_pass<T, 5, S, VMAX>(L, logC, get, put); break;
+    default: first_pass<T, 8, S, VMAX>(L, logC, get, put); break;
+  }
+}
+
+template <typename T, int S, int VMAX, typename Put>
+__device__ __forceinline__ void last_pass_any(int R, const cx<T> *lds, int L, int logC, int twstep,
+                                              const cx<T> *__restrict__ tw, Put put) {
+  switch (R) {
+    case 2: last_pass<T, 2, S, VMAX>(lds, L, logC, twstep, tw, put); break;
+    case 4: last_pass<T, 4, S, VMAX>(lds, L, logC, twstep, tw, put); break;
+    case 5: last_pass<T, 5, S, VMAX>(lds, L, logC, twstep, tw, put); break;
+    default: last_pass<T, 8, S, VMAX>(lds, L, logC, twstep, tw, put); break;
+  }
+}
+
+// Element at base + index. OFF32: the index fits 32 bits in bytes, so the
+// address is a uniform base plus one 32-bit per-lane offset (one VGPR per
+// load in flight instead of a 64-bit address pair).
+template <bool OFF32, typename E>
+__device__ __forceinline__ E load_elem(const E *base, int64_t index) {
+  if constexpr (OFF32)
+    return *reinterpret_cast<const E *>(reinterpret_cast<const char *>(base) +
+                                        static_cast<uint32_t>(index) * static_cast<uint32_t>(sizeof(E)));
+  else
+    return base[index];
+}
+template <bool OFF32, typename E>
+__device__ __forceinline__ void store_elem(E *base, int64_t index, E v) {
+  if constexpr (OFF32)
+    *reinterpret_cast<E *>(reinterpret_cast<char *>(base) +
+                           static_cast<uint32_t>(index) * static_cast<uint32_t>(sizeof(E))) = v;
+  else
+    base[index] = v;
+}
+
 template <typename T, typename Src, bool ROUND>
-__device__ __forceinline__ T load_sample(const Src *p) {
-  Src v = *p;
+__device__ __forceinline__ T to_compute(Src v) {
   if constexpr (ROUND && sizeof(Src) == 8) return static_cast<T>(round_f32(v));
   return static_cast<T>(v);
 }
 
 // --------------------------------------------------------------- forward
-template <typename T, typename Src, bool ROUND>
+template <typename T, typename Src, bool ROUND, int VMAX, bool OFF32>
 __global__ __launch_bounds__(kBlock) void rfft_forward_kernel(FftGeom g, FwdFftArgs a, int logC,
-                                                              const cx<T> *__restrict__ tw) {
+                                                              const cx<T> *__restrict__ tw, int64_t nblocks) {
   extern __shared__ __align__(16) unsigned char smem[];
   cx<T> *lds = reinterpret_cast<cx<T> *>(smem);
   const int C = 1 << logC;
   const int L = g.L;
   const int c = threadIdx.x & (C - 1);  // fixed per thread: kBlock is a multiple of C
-  const int64_t ch = static_cast<int64_t>(blockIdx.x) * C + c;
+  const int64_t ch = xcd_contiguous_block(blockIdx.x, nblocks) * C + c;
   const bool live = ch < a.nchan;
-  const Src *src = static_cast<const Src *>(a.src) + ch;
+  const Src *src = static_cast<const Src *>(a.src);
+  const int64_t Nt = a.Nt, ld = a.src_ld;
 
   // stages 1-2 boundary: packed samples z[n] = x[2n] + i x[2n+1]; samples at
   // t >= Nt are the zero padding and are not read
-  for (int b = threadIdx.x; b < (L << logC); b += kBlock) {
-    int64_t t0 = 2 * static_cast<int64_t>(b >> logC);
+  auto get = [&](int n) {
+    const int64_t t0 = 2 * static_cast<int64_t>(n);
     T re = T(0), im = T(0);
-    if (live && t0 < a.Nt) re = load_sample<T, Src, ROUND>(src + t0 * a.src_ld);
-    if (live && t0 + 1 < a.Nt) im = load_sample<T, Src, ROUND>(src + (t0 + 1) * a.src_ld);
-    lds[b] = mk(re, im);
+    if (live && t0 < Nt) re = to_compute<T, Src, ROUND>(load_elem<OFF32>(src, t0 * ld + ch));
+    if (live && t0 + 1 < Nt) im = to_compute<T, Src, ROUND>(load_elem<OFF32>(src, (t0 + 1) * ld + ch));
+    return mk(re, im);
+  };
+  auto to_lds = [&](int n, cx<T> v) { lds[(n << logC) + c] = v; };
+  if (g.npass == 0) {  // L == 1
+    if (threadIdx.x < C) to_lds(0, get(0));
+  } else {
+    first_pass_any<T, -1, VMAX>(g.radix[0], L, logC, get, to_lds);
   }
   __syncthreads();
-  all_passes<T, -1>(lds, g, logC, tw);
+  middle_passes<T, -1, VMAX>(lds, g, 1, g.npass, logC, tw);
 
   if (!live) return;
   const int64_t row = ch / a.cpr, col = ch - row * a.cpr;
@@ -214,65 +323,72 @@ __global__ __launch_bounds__(kBlock) void rfft_forward_kernel(FftGeom g, FwdFftA
 }
 
 // --------------------------------------------------------------- inverse
-template <typename T, typename Src>
+template <typename T, typename Src, int VMAX, bool OFF32>
 __global__ __launch_bounds__(kBlock) void rfft_inverse_kernel(FftGeom g, InvFftArgs a, int logC,
-                                                              const cx<T> *__restrict__ tw, T inv_l) {
+                                                              const cx<T> *__restrict__ tw, T inv_l,
+                                                              int64_t nblocks) {
   extern __shared__ __align__(16) unsigned char smem[];
   cx<T> *lds = reinterpret_cast<cx<T> *>(smem);
   const int C = 1 << logC;
   const int L = g.L;
   const int c = threadIdx.x & (C - 1);
-  const int64_t ch = static_cast<int64_t>(blockIdx.x) * C + c;
+  const int64_t ch = xcd_contiguous_block(blockIdx.x, nblocks) * C + c;
   const bool live = ch < a.nchan;
-  const cx<Src> *src = static_cast<const cx<Src> *>(a.src) + ch;
+  const cx<Src> *src = static_cast<const cx<Src> *>(a.src);
+  const int64_t Nt = a.Nt, ld = a.src_ld, dld = a.dst_ld;
 
   // Z[k] = E[k] + i O[k] with E = (X[k] + conj X[L-k]) / 2 and
   // O = (X[k] - conj X[L-k]) conj(w^k) / 2; the imaginary parts of bins 0
   // and L (= Nt) are dropped, as a real signal's spectrum has none
-  for (int b = threadIdx.x; b < (L << logC); b += kBlock) {
-    int k = b >> logC;
-    cx<T> z = mk(T(0), T(0));
-    if (live) {
-      cx<T> xa = cvt<T>(src[static_cast<int64_t>(k) * a.src_ld]);
-      cx<T> xb = cvt<T>(src[static_cast<int64_t>(L - k) * a.src_ld]);
-      if (k == 0) {
-        xa.im = T(0);
-        xb.im = T(0);
-      }
-      xb = conj(xb);
-      cx<T> e = scale(xa + xb, T(0.5));
-      cx<T> o = scale(cmulc(xa - xb, tw[k]), T(0.5));
-      z = mk(e.re - o.im, e.im + o.re);
+  auto get = [&](int k) {
+    if (!live) return mk(T(0), T(0));
+    cx<T> xa = cvt<T>(load_elem<OFF32>(src, static_cast<int64_t>(k) * ld + ch));
+    cx<T> xb = cvt<T>(load_elem<OFF32>(src, static_cast<int64_t>(L - k) * ld + ch));
+    if (k == 0) {
+      xa.im = T(0);
+      xb.im = T(0);
     }
-    lds[b] = z;
-  }
-  __syncthreads();
-  all_passes<T, +1>(lds, g, logC, tw);
-
-  if (!live) return;
+    xb = conj(xb);
+    cx<T> e = scale(xa + xb, T(0.5));
+    cx<T> o = scale(cmulc(xa - xb, tw[k]), T(0.5));
+    return mk(e.re - o.im, e.im + o.re);
+  };
   // stage 4-5 boundary: z[n] = y[2n] + i y[2n+1]; keep t < Nt only
-  const int64_t half = (a.Nt + 1) / 2;
-  for (int b = threadIdx.x; b < (half << logC); b += kBlock) {
-    int64_t n = b >> logC;
-    cx<T> z = lds[b];
-    T y0 = z.re * inv_l, y1 = z.im * inv_l;
-    int64_t t0 = 2 * n;
-    bool second = t0 + 1 < a.Nt;
+  auto put = [&](int n, cx<T> z) {
+    const int64_t t0 = 2 * static_cast<int64_t>(n);
+    if (!live || t0 >= Nt) return;
+    const bool second = t0 + 1 < Nt;
+    const T y0 = z.re * inv_l, y1 = z.im * inv_l;
     if (a.dst_f32) {
-      float *d = static_cast<float *>(a.dst) + ch;
-      d[t0 * a.dst_ld] = static_cast<float>(y0);
-      if (second) d[(t0 + 1) * a.dst_ld] = static_cast<float>(y1);
+      float *d = static_cast<float *>(a.dst);
+      store_elem<OFF32>(d, t0 * dld + ch, static_cast<float>(y0));
+      if (second) store_elem<OFF32>(d, (t0 + 1) * dld + ch, static_cast<float>(y1));
     } else {
-      double *d = static_cast<double *>(a.dst) + ch;
+      double *d = static_cast<double *>(a.dst);
       double v0 = static_cast<double>(y0), v1 = static_cast<double>(y1);
       if (a.round_f32) {
         v0 = round_f32(v0);
         v1 = round_f32(v1);
       }
-      d[t0 * a.dst_ld] = v0;
-      if (second) d[(t0 + 1) * a.dst_ld] = v1;
+      store_elem<OFF32>(d, t0 * dld + ch, v0);
+      if (second) store_elem<OFF32>(d, (t0 + 1) * dld + ch, v1);
     }
+  };
+  auto to_lds = [&](int n, cx<T> v) { lds[(n << logC) + c] = v; };
+
+  if (g.npass == 0) {  // L == 1
+    if (threadIdx.x < C) put(0, get(0));
+    return;
   }
+  if (g.npass == 1) {
+    first_pass_any<T, +1, VMAX>(g.radix[0], L, logC, get, put);
+    return;
+  }
+  first_pass_any<T, +1, VMAX>(g.radix[0], L, logC, get, to_lds);
+  __syncthreads();
+  middle_passes<T, +1, VMAX>(lds, g, 1, g.npass - 1, logC, tw);
+  const int pl = g.npass - 1;
+  last_pass_any<T, +1, VMAX>(g.radix[pl], lds, L, logC, g.twstep[pl], tw, put);
 }
 
 int ilog2(int c) {
@@ -283,74 +399,118 @@ int ilog2(int c) {
 
 }  // namespace
 
-int fft_channels_per_block(const FftGeom &g, bool f32, int64_t nchan) {
+// (channels per workgroup, VMAX) for a schedule, precision and batch: the
+// widest C that still gives at least 1024 workgroups (four per CU), with the
+// smaller register budget when it fits; for small batches the narrowest C
+// (most workgroups). C = 0 when the transform does not fit at all.
+FftLaunch fft_launch_config(const FftGeom &g, bool f32, int64_t nchan) {
   const int64_t esz = f32 ? 8 : 16;
-  int best = 0;
-  for (int C = kMaxChannelsPerBlock; C >= 1; C >>= 1) {
-    if (static_cast<int64_t>(g.L) * C * esz > kMaxLds) continue;
-    bool ok = true;
+  auto fits = [&](int C, int vmax) {
+    if (static_cast<int64_t>(g.L) * C * esz > kMaxLds) return false;
     for (int p = 0; p < g.npass; ++p) {
-      int64_t nb = static_cast<int64_t>(g.L / g.radix[p]) * C;
-      if (nb > static_cast<int64_t>(host_butterflies_per_thread(f32, g.radix[p])) * kBlock) ok = false;
+      const int64_t nb = static_cast<int64_t>(g.L / g.radix[p]) * C;
+      if (nb > static_cast<int64_t>(vmax / g.radix[p]) * kBlock) return false;
     }
-    if (ok) {
-      best = C;
-      break;
-    }
+    return true;
+  };
+  FftLaunch narrowest;
+  for (int C = kMaxChannelsPerBlock; C >= 1; C >>= 1) {
+    const int vmax = fits(C, kVmaxSmall) ? kVmaxSmall : fits(C, kVmaxLarge) ? kVmaxLarge : 0;
+    if (vmax == 0) continue;
+    if ((nchan + C - 1) / C >= 1024) return {C, vmax};
+    narrowest = {C, vmax};
   }
-  // Prefer more, narrower workgroups while the batch would not fill the GPU.
-  while (best > 1 && (nchan + best - 1) / best < 512) best >>= 1;
-  return best;
+  return narrowest;
 }
+
+int fft_channels_per_block(const FftGeom &g, bool f32, int64_t nchan) { return fft_launch_config(g, f32, nchan).C; }
+
+namespace {
+
+// byte extent below 4 GiB: 32-bit offsets are exact
+bool fits_32bit(int64_t rows, int64_t ld, int64_t esz) { return rows * ld * esz < (int64_t(1) << 32); }
+
+template <typename T, typename Src, bool ROUND>
+void fwd(const FftGeom &g, const FwdFftArgs &a, const FftLaunch &cfg, const void *tw, hipStream_t s) {
+  const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
+  const size_t lds = static_cast<size_t>(g.L) * cfg.C * sizeof(cx<T>);
+  auto twp = static_cast<const cx<T> *>(tw);
+  const int logC = ilog2(cfg.C);
+  const dim3 grid(static_cast<unsigned>(nblocks));
+  const bool off32 = fits_32bit(a.Nt, a.src_ld, sizeof(Src));
+  if (cfg.vmax == kVmaxSmall && off32)
+    hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmaxSmall, true>), grid, dim3(kBlock), lds, s, g, a,
+                       logC, twp, nblocks);
+  else if (cfg.vmax == kVmaxSmall)
+    hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmaxSmall, false>), grid, dim3(kBlock), lds, s, g, a,
+                       logC, twp, nblocks);
+  else if (off32)
+    hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmaxLarge, true>), grid, dim3(kBlock), lds, s, g, a,
+                       logC, twp, nblocks);
+  else
+    hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmaxLarge, false>), grid, dim3(kBlock), lds, s, g, a,
+                       logC, twp, nblocks);
+}
+
+template <typename T, typename Src>
+void inv(const FftGeom &g, const InvFftArgs &a, const FftLaunch &cfg, const void *tw, hipStream_t s) {
+  const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
+  const size_t lds = static_cast<size_t>(g.L) * cfg.C * sizeof(cx<T>);
+  auto twp = static_cast<const cx<T> *>(tw);
+  const T inv_l = T(1) / static_cast<T>(g.L);
+  const int logC = ilog2(cfg.C);
+  const dim3 grid(static_cast<unsigned>(nblocks));
+  const bool off32 = fits_32bit(g.L + 1, a.src_ld, sizeof(cx<Src>)) && fits_32bit(a.Nt, a.dst_ld, 8);
+  if (cfg.vmax == kVmaxSmall && off32)
+    hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmaxSmall, true>), grid, dim3(kBlock), lds, s, g, a, logC, twp,
+                       inv_l, nblocks);
+  else if (cfg.vmax == kVmaxSmall)
+    hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmaxSmall, false>), grid, dim3(kBlock), lds, s, g, a, logC,
+                       twp, inv_l, nblocks);
+  else if (off32)
+    hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmaxLarge, true>), grid, dim3(kBlock), lds, s, g, a, logC, twp,
+                       inv_l, nblocks);
+  else
+    hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmaxLarge, false>), grid, dim3(kBlock), lds, s, g, a, logC,
+                       twp, inv_l, nblocks);
+}
+
+}  // namespace
 
 hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s) {
-  const int C = fft_channels_per_block(g, compute_f32, a.nchan);
-  if (C == 0) return hipErrorInvalidValue;
-  const int logC = ilog2(C);
-  const dim3 grid(static_cast<unsigned>((a.nchan + C - 1) / C));
+  const FftLaunch cfg = fft_launch_config(g, compute_f32, a.nchan);
+  if (cfg.C == 0 || (a.nchan + cfg.C - 1) / cfg.C > INT32_MAX) return hipErrorInvalidValue;
   if (compute_f32) {
-    const size_t lds = static_cast<size_t>(g.L) * C * sizeof(cx<float>);
-    auto twp = static_cast<const cx<float> *>(tw);
     if (a.src_f32)
-      hipLaunchKernelGGL((rfft_forward_kernel<float, float, false>), grid, dim3(kBlock), lds, s, g, a, logC, twp);
+      fwd<float, float, false>(g, a, cfg, tw, s);
     else
-      hipLaunchKernelGGL((rfft_forward_kernel<float, double, false>), grid, dim3(kBlock), lds, s, g, a, logC, twp);
+      fwd<float, double, false>(g, a, cfg, tw, s);
   } else {
-    const size_t lds = static_cast<size_t>(g.L) * C * sizeof(cx<double>);
-    auto twp = static_cast<const cx<double> *>(tw);
     if (a.src_f32)
-      hipLaunchKernelGGL((rfft_forward_kernel<double, float, false>), grid, dim3(kBlock), lds, s, g, a, logC, twp);
+      fwd<double, float, false>(g, a, cfg, tw, s);
     else if (a.round_f32)
-      hipLaunchKernelGGL((rfft_forward_kernel<double, double, true>), grid, dim3(kBlock), lds, s, g, a, logC, twp);
+      fwd<double, double, true>(g, a, cfg, tw, s);
     else
-      hipLaunchKernelGGL((rfft_forward_kernel<double, double, false>), grid, dim3(kBlock), lds, s, g, a, logC, twp);
+      fwd<double, double, false>(g, a, cfg, tw, s);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_fft_inverse(const FftGeom &g, const InvFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s) {
-  const int C = fft_channels_per_block(g, compute_f32, a.nchan);
-  if (C == 0) return hipErrorInvalidValue;
-  const int logC = ilog2(C);
-  const dim3 grid(static_cast<unsigned>((a.nchan + C - 1) / C));
+  const FftLaunch cfg = fft_launch_config(g, compute_f32, a.nchan);
+  if (cfg.C == 0 || (a.nchan + cfg.C - 1) / cfg.C > INT32_MAX) return hipErrorInvalidValue;
   if (compute_f32) {
-    const size_t lds = static_cast<size_t>(g.L) * C * sizeof(cx<float>);
-    auto twp = static_cast<const cx<float> *>(tw);
-    const float inv_l = 1.0f / static_cast<float>(g.L);
     if (a.src_f32)
-      hipLaunchKernelGGL((rfft_inverse_kernel<float, float>), grid, dim3(kBlock), lds, s, g, a, logC, twp, inv_l);
+      inv<float, float>(g, a, cfg, tw, s);
     else
-      hipLaunchKernelGGL((rfft_inverse_kernel<float, double>), grid, dim3(kBlock), lds, s, g, a, logC, twp, inv_l);
+      inv<float, double>(g, a, cfg, tw, s);
   } else {
-    const size_t lds = static_cast<size_t>(g.L) * C * sizeof(cx<double>);
-    auto twp = static_cast<const cx<double> *>(tw);
-    const double inv_l = 1.0 / static_cast<double>(g.L);
     if (a.src_f32)
-      hipLaunchKernelGGL((rfft_inverse_kernel<double, float>), grid, dim3(kBlock), lds, s, g, a, logC, twp, inv_l);
+      inv<double, float>(g, a, cfg, tw, s);
     else
-      hipLaunchKernelGGL((rfft_inverse_kernel<double, double>), grid, dim3(kBlock), lds, s, g, a, logC, twp, inv_l);
+      inv<double, double>(g, a, cfg, tw, s);
   }
   return hipGetLastError();
 }

@@ -72,8 +72,15 @@ struct CastArgs {
   bool dst_f32 = false;
 };
 
-// Channels per FFT workgroup for this schedule, precision and batch size
-// (power of two, fits LDS and the per-thread butterfly budget); 0 if none.
+// FFT launch shape: C channels per workgroup (power of two) and the
+// per-thread register budget VMAX (complex values held during a pass).
+struct FftLaunch {
+  int C = 0;
+  int vmax = 0;
+};
+FftLaunch fft_launch_config(const FftGeom &g, bool f32, int64_t nchan);
+// Channels per FFT workgroup for this schedule, precision and batch size; 0
+// if the transform does not fit.
 int fft_channels_per_block(const FftGeom &g, bool f32, int64_t nchan);
 
 hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,

@@ -45,6 +45,14 @@ __device__ __forceinline__ void split(const f64x2 &f, cx<double> *o) { o[0] = mk
 __device__ __forceinline__ f32x4 load_stream(const f32x4 *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ f64x2 load_stream(const f64x2 *p) { return __builtin_nontemporal_load(p); }
 
+// base[off] with a wave-uniform base and a 32-bit byte offset: lets the
+// compiler use the scalar-base + 32-bit vector-offset form of the load and
+// keeps one VGPR per address instead of two.
+template <typename V>
+__device__ __forceinline__ V load_stream_at(const V *base, uint32_t byte_off) {
+  return load_stream(reinterpret_cast<const V *>(reinterpret_cast<const char *>(base) + byte_off));
+}
+
 // The Vec16<T>::n complex entries of the input vector that line up with
 // 16-byte vector j of a row, converted to T.
 template <typename T, typename In>
@@ -58,6 +66,27 @@ __device__ __forceinline__ void load_x(const cx<In> *__restrict__ x, int64_t j, 
   }
 }
 
+// The Vec16<T>::n consecutive complex outputs at y[idx..], one store per
+// 16 bytes (idx is a multiple of n and rows of y have even length).
+template <typename T>
+__device__ __forceinline__ void store_vec(void *y, int64_t idx, bool f32, const cx<T> *v) {
+  if constexpr (sizeof(T) == 4) {
+    if (f32) {
+      f32x4 w = {v[0].re, v[0].im, v[1].re, v[1].im};
+      *reinterpret_cast<f32x4 *>(static_cast<cx<float> *>(y) + idx) = w;
+    } else {
+      f64x2 *d = reinterpret_cast<f64x2 *>(static_cast<cx<double> *>(y) + idx);
+      d[0] = f64x2{v[0].re, v[0].im};
+      d[1] = f64x2{v[1].re, v[1].im};
+    }
+  } else {
+    if (f32)
+      static_cast<cx<float> *>(y)[idx] = cvt<float>(v[0]);
+    else
+      *reinterpret_cast<f64x2 *>(static_cast<cx<double> *>(y) + idx) = f64x2{v[0].re, v[0].im};
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store_y(void *y, int64_t idx, bool f32, cx<T> v) {
   if (f32)
@@ -66,23 +95,45 @@ __device__ __forceinline__ void store_y(void *y, int64_t idx, bool f32, cx<T> v)
     static_cast<cx<double> *>(y)[idx] = cvt<double>(v);
 }
 
+// acc += f * x (F) and acc += conj(f) * x (F*), one FMA per real product so
+// that each partial sum is a plain FMA chain.
+template <typename T>
+__device__ __forceinline__ void fma_mul(T &re, T &im, cx<T> f, cx<T> x) {
+  re = fma(f.re, x.re, re);
+  re = fma(-f.im, x.im, re);
+  im = fma(f.re, x.im, im);
+  im = fma(f.im, x.re, im);
+}
+template <typename T>
+__device__ __forceinline__ void fma_conj_mul(T &re, T &im, cx<T> f, cx<T> x) {
+  re = fma(f.re, x.re, re);
+  re = fma(f.im, x.im, re);
+  im = fma(f.re, x.im, im);
+  im = fma(-f.im, x.re, im);
+}
+
 // ------------------------------------------------------------------ F
 // v_k[r] = sum_c Fhat_k[r][c] m_k[c].
 // One wave per task = (frequency k, R consecutive rows). The wave walks the
 // rows side by side: lane l takes 16-byte vectors l, l+64, ... of each row,
 // so each load instruction reads 1 KiB contiguous per row, and the matching
 // piece of m_k is loaded once for all R rows. U vectors per row are in flight
-// per step. Per-lane partial sums are closed with wave_sum (DPP).
+// per step (R*U Fhat loads issued before any arithmetic). Per-lane partial
+// sums are closed with wave_sum (DPP).
 template <typename T, typename In, int R, int U>
-__global__ __launch_bounds__(kBlock) void sbgemv_n_kernel(const typename Vec16<T>::type *__restrict__ F,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void sbgemv_n_kernel(const typename Vec16<T>::type *__restrict__ F,
                                                           const cx<In> *__restrict__ x, void *__restrict__ y,
                                                           int64_t Nd, int64_t ldF_vec, int64_t nvec, int64_t ldx,
                                                           int64_t ldy, bool y_f32, int64_t ngroups, int64_t ntasks,
                                                           int64_t nblocks) {
   using V = typename Vec16<T>::type;
   constexpr int NV = Vec16<T>::n;
+  constexpr int NC = U * NV;  // chains per row and lane
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t task = xcd_contiguous_block(blockIdx.x, nblocks) * (kBlock / kWave) + (threadIdx.x / kWave);
+  // the wave index is uniform across the wave: say so, so that the task,
+  // the row pointers and the loop bounds live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t task = xcd_contiguous_block(blockIdx.x, nblocks) * (kBlock / kWave) + wave;
   if (task >= ntasks) return;
   const int64_t k = task / ngroups;
   const int64_t r0 = (task - k * ngroups) * R;
@@ -95,22 +146,21 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_kernel(const typename Vec16<T
   }
   const cx<In> *xk = x + k * ldx;
 
-  cx<T> acc[R][U][NV];
+  T ar[R][NC], ai[R][NC];
 #pragma unroll
   for (int i = 0; i < R; ++i)
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int e = 0; e < NV; ++e) acc[i][u][e] = mk(T(0), T(0));
+    for (int c = 0; c < NC; ++c) ar[i][c] = ai[i][c] = T(0);
 
   int64_t j = lane;
   for (; j + (U - 1) * kWave < nvec; j += U * kWave) {
-    cx<T> xv[U][NV];
     V fv[U][R];
+    cx<T> xv[U][NV];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < R; ++i) fv[u][i] = load_stream(rows[i] + j + u * kWave);
+      for (int i = 0; i < R; ++i)
+        fv[u][i] = load_stream_at(rows[i], static_cast<uint32_t>(j + u * kWave) * static_cast<uint32_t>(sizeof(V)));
 #pragma unroll
     for (int u = 0; u < U; ++u) load_x<T, In>(xk, j + u * kWave, xv[u]);
 #pragma unroll
@@ -120,103 +170,160 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_kernel(const typename Vec16<T
         cx<T> f[NV];
         split(fv[u][i], f);
 #pragma unroll
-        for (int e = 0; e < NV; ++e) acc[i][u][e] = acc[i][u][e] + cmul(f[e], xv[u][e]);
+        for (int e = 0; e < NV; ++e) fma_mul(ar[i][u * NV + e], ai[i][u * NV + e], f[e], xv[u][e]);
       }
   }
-  for (; j < nvec; j += kWave) {
+  for (; j < nvec; j += kWave) {  // fewer than U vectors left in the row
     cx<T> xv[NV];
     load_x<T, In>(xk, j, xv);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       cx<T> f[NV];
-      split(load_stream(rows[i] + j), f);
+      split(load_stream_at(rows[i], static_cast<uint32_t>(j) * static_cast<uint32_t>(sizeof(V))), f);
 #pragma unroll
-      for (int e = 0; e < NV; ++e) acc[i][0][e] = acc[i][0][e] + cmul(f[e], xv[e]);
+      for (int e = 0; e < NV; ++e) fma_mul(ar[i][e], ai[i][e], f[e], xv[e]);
     }
   }
 
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    // pairwise tree over the U*NV chains of this lane
-    cx<T> part[U * NV];
+    // pairwise tree over this lane's chains, then across the wave
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int w = 1; w < NC; w *= 2)
 #pragma unroll
-      for (int e = 0; e < NV; ++e) part[u * NV + e] = acc[i][u][e];
-#pragma unroll
-    for (int w = 1; w < U * NV; w *= 2)
-#pragma unroll
-      for (int q = 0; q + w < U * NV; q += 2 * w) part[q] = part[q] + part[q + w];
-    cx<T> s = mk(wave_sum(part[0].re), wave_sum(part[0].im));
+      for (int q = 0; q + w < NC; q += 2 * w) {
+        ar[i][q] += ar[i][q + w];
+        ai[i][q] += ai[i][q + w];
+      }
+    cx<T> s = mk(wave_sum(ar[i][0]), wave_sum(ai[i][0]));
     if (lane == 0 && r0 + i < Nd) store_y(y, k * ldy + r0 + i, y_f32, s);
   }
 }
 
 // ------------------------------------------------------------------ F*
 // w_k[c] = sum_r conj(Fhat_k[r][c]) d_k[r].
-// One workgroup per (frequency k, 256 consecutive 16-byte column vectors):
-// each lane owns one vector (two complex64 columns or one complex128 column)
-// and walks down all Nd rows, U rows in flight; no cross-lane reduction.
-// d_k[r] is the same for the whole workgroup (a uniform load). Row r feeds
-// chain r mod U (the last Nd mod U rows feed chain 0), and the U chains are
-// closed with a tree.
-template <typename T, typename In, int U>
-__global__ __launch_bounds__(kBlock) void sbgemv_c_kernel(const typename Vec16<T>::type *__restrict__ F,
-                                                          const cx<In> *__restrict__ x, void *__restrict__ y,
-                                                          int64_t Nd, int64_t ldF_vec, int64_t nvec, int64_t ldx,
-                                                          int64_t ldy, bool y_f32, int64_t nchunks, int64_t nblocks) {
+// One workgroup per (frequency k, chunk of VL*256 consecutive 16-byte column
+// vectors): each lane owns VL vectors 256 apart (a vector is two complex64
+// columns or one complex128 column) and walks down all Nd rows with U rows
+// in flight, so the workgroup reads VL*4 KiB contiguous of each row per step;
+// no cross-lane reduction. The host picks VL so that a frequency splits into
+// chunks of nearly equal size. d_k[r] is the same for the whole workgroup (a
+// scalar load). Row r feeds chain (r mod U) mod S (the last Nd mod U rows
+// feed chain 0), and the S chains are added at the end.
+template <typename T, typename In, int VL, int U, int S>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void sbgemv_c_kernel(
+    const typename Vec16<T>::type *__restrict__ F, const cx<In> *__restrict__ x, void *__restrict__ y, int64_t Nd,
+    int64_t ldF_vec, int64_t nvec, int64_t ldx, int64_t ldy, bool y_f32, int64_t nchunks, int64_t nblocks) {
   using V = typename Vec16<T>::type;
   constexpr int NV = Vec16<T>::n;
   const int64_t blk = xcd_contiguous_block(blockIdx.x, nblocks);
   const int64_t k = blk / nchunks;
-  const int64_t j = (blk - k * nchunks) * kBlock + threadIdx.x;
-  const bool valid = j < nvec;
-  const V *col = F + k * Nd * ldF_vec + (valid ? j : nvec - 1);
+  const int64_t j0 = (blk - k * nchunks) * (kBlock * VL) + threadIdx.x;
+  const V *base = F + k * Nd * ldF_vec;
   const cx<In> *xk = x + k * ldx;
-
-  cx<T> acc[U][NV];
+  uint32_t off[VL];  // byte offsets within a row (rows are far below 4 GiB)
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int e = 0; e < NV; ++e) acc[u][e] = mk(T(0), T(0));
+  for (int v = 0; v < VL; ++v) {
+    int64_t j = j0 + v * kBlock;
+    j = j < nvec ? j : nvec - 1;  // lanes past the end re-read the last vector, never store
+    off[v] = static_cast<uint32_t>(j) * static_cast<uint32_t>(sizeof(V));
+  }
 
+  T ar[S][VL][NV], ai[S][VL][NV];
+#pragma unroll
+  for (int c = 0; c < S; ++c)
+#pragma unroll
+    for (int v = 0; v < VL; ++v)
+#pragma unroll
+      for (int e = 0; e < NV; ++e) ar[c][v][e] = ai[c][v][e] = T(0);
+
+  // Per step: the U rows of one column group are loaded together, then
+  // used; measured faster than putting all U*VL loads in flight at once
+  // (fewer distinct DRAM rows open per wave).
   int64_t r = 0;
   for (; r + U <= Nd; r += U) {
-    V fv[U];
+    cx<T> d[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) fv[u] = load_stream(col + (r + u) * ldF_vec);
+    for (int u = 0; u < U; ++u) d[u] = cvt<T>(xk[r + u]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      cx<T> d = cvt<T>(xk[r + u]);
-      cx<T> f[NV];
-      split(fv[u], f);
+    for (int v = 0; v < VL; ++v) {
+      V fv[U];
 #pragma unroll
-      for (int e = 0; e < NV; ++e) acc[u][e] = acc[u][e] + cmulc(d, f[e]);
+      for (int u = 0; u < U; ++u) fv[u] = load_stream_at(base + (r + u) * ldF_vec, off[v]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        cx<T> f[NV];
+        split(fv[u], f);
+#pragma unroll
+        for (int e = 0; e < NV; ++e) fma_conj_mul(ar[u % S][v][e], ai[u % S][v][e], f[e], d[u]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the next group's loads after this group's use
     }
   }
   for (; r < Nd; ++r) {  // fewer than U rows left
     cx<T> d = cvt<T>(xk[r]);
-    cx<T> f[NV];
-    split(load_stream(col + r * ldF_vec), f);
 #pragma unroll
-    for (int e = 0; e < NV; ++e) acc[0][e] = acc[0][e] + cmulc(d, f[e]);
+    for (int v = 0; v < VL; ++v) {
+      cx<T> f[NV];
+      split(load_stream_at(base + r * ldF_vec, off[v]), f);
+#pragma unroll
+      for (int e = 0; e < NV; ++e) fma_conj_mul(ar[0][v][e], ai[0][v][e], f[e], d);
+    }
   }
 
 #pragma unroll
-  for (int w = 1; w < U; w *= 2)
+  for (int v = 0; v < VL; ++v) {
+    const int64_t j = j0 + v * kBlock;
+    if (j < nvec) {
+      cx<T> out[NV];
 #pragma unroll
-    for (int q = 0; q + w < U; q += 2 * w)
+      for (int e = 0; e < NV; ++e) {
+        T sr = ar[0][v][e], si = ai[0][v][e];
 #pragma unroll
-      for (int e = 0; e < NV; ++e) acc[q][e] = acc[q][e] + acc[q + w][e];
-  if (valid) {
-#pragma unroll
-    for (int e = 0; e < NV; ++e) store_y(y, k * ldy + j * NV + e, y_f32, acc[0][e]);
+        for (int c = 1; c < S; ++c) {
+          sr += ar[c][v][e];
+          si += ai[c][v][e];
+        }
+        out[e] = mk(sr, si);
+      }
+      store_vec(y, k * ldy + j * NV, y_f32, out);
+    }
   }
 }
 
-constexpr int kRowsN = 4;     // rows per wave, F direction
-constexpr int kUnrollN = 2;   // vectors per row in flight, F direction
-constexpr int kUnrollC = 8;   // rows in flight, F* direction
+constexpr int kRowsN = 4;    // rows per wave, F direction
+constexpr int kUnrollN = 2;  // vectors per row in flight, F direction
+constexpr int kMaxVecsC = 5;  // vectors per lane, F* direction (at most)
+constexpr int kChainsC = 2;   // accumulator chains per column, F* direction
+// rows in flight, F* direction: VL*U loads stay under the register budget
+// of four waves per SIMD
+constexpr int unroll_c(int vl) { return vl >= 4 ? 2 : 4; }
+
+template <typename T, typename In, int VL>
+void launch_c(const SbgemvArgs &a, int64_t nvec, int64_t nchunks, hipStream_t s) {
+  using V = typename Vec16<T>::type;
+  const int nv = Vec16<T>::n;
+  const int64_t nblocks = a.K * nchunks;
+  hipLaunchKernelGGL((sbgemv_c_kernel<T, In, VL, unroll_c(VL), kChainsC>), dim3(static_cast<unsigned>(nblocks)),
+                     dim3(kBlock), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
+                     a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks);
+}
+
+template <typename T, typename In>
+void launch_c_vl(const SbgemvArgs &a, int64_t nvec, hipStream_t s) {
+  // fewest chunks of at most kMaxVecsC*256 vectors, then the smallest VL
+  // that still covers the row: chunks of (nearly) equal length
+  const int64_t nchunks = (nvec + kBlock * kMaxVecsC - 1) / (kBlock * kMaxVecsC);
+  const int64_t vl = (nvec + nchunks * kBlock - 1) / (nchunks * kBlock);
+  const int64_t nch = (nvec + vl * kBlock - 1) / (vl * kBlock);
+  switch (vl) {
+    case 1: launch_c<T, In, 1>(a, nvec, nch, s); break;
+    case 2: launch_c<T, In, 2>(a, nvec, nch, s); break;
+    case 3: launch_c<T, In, 3>(a, nvec, nch, s); break;
+    case 4: launch_c<T, In, 4>(a, nvec, nch, s); break;
+    default: launch_c<T, In, 5>(a, nvec, nch, s); break;
+  }
+}
 
 }  // namespace
 
@@ -247,23 +354,12 @@ hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
 hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s) {
   const int nv = compute_f32 ? 2 : 1;
   const int64_t nvec = (a.Nm + nv - 1) / nv;
-  const int64_t nchunks = (nvec + kBlock - 1) / kBlock;
-  const int64_t nblocks = a.K * nchunks;
-  const dim3 grid(static_cast<unsigned>(nblocks)), block(kBlock);
-  const int64_t ldF_vec = a.ldF / nv;
-  if (compute_f32) {
-    hipLaunchKernelGGL((sbgemv_c_kernel<float, float, kUnrollC>), grid, block, 0, s,
-                       static_cast<const f32x4 *>(a.F), static_cast<const cx<float> *>(a.x), a.y, a.Nd, ldF_vec, nvec,
-                       a.ldx, a.ldy, a.y_f32, nchunks, nblocks);
-  } else if (a.x_f32) {
-    hipLaunchKernelGGL((sbgemv_c_kernel<double, float, kUnrollC>), grid, block, 0, s,
-                       static_cast<const f64x2 *>(a.F), static_cast<const cx<float> *>(a.x), a.y, a.Nd, ldF_vec,
-                       nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks);
-  } else {
-    hipLaunchKernelGGL((sbgemv_c_kernel<double, double, kUnrollC>), grid, block, 0, s,
-                       static_cast<const f64x2 *>(a.F), static_cast<const cx<double> *>(a.x), a.y, a.Nd, ldF_vec,
-                       nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks);
-  }
+  if (compute_f32)
+    launch_c_vl<float, float>(a, nvec, s);
+  else if (a.x_f32)
+    launch_c_vl<double, float>(a, nvec, s);
+  else
+    launch_c_vl<double, double>(a, nvec, s);
   return hipGetLastError();
 }
 
