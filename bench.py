@@ -26,6 +26,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "sbgemv_n_main_mixed_traffic.json")
+
+
+def measured_traffic(Nm, Nd, Nt, mask):
+    """HBM bytes per sbgemv_n launch from the committed rocprofv3 counter
+    record (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None if
+    the record is for another workload or the kernel sources changed since
+    the counters were taken."""
+    import hashlib
+
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != f"Nm={Nm} Nd={Nd} Nt={Nt} mask {mask:#05x}":
+        return None
+    h = hashlib.sha256()
+    for rel in rec.get("sources", []):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec.get("sources_sha256"):
+        return None
+    return int(round(rec["traffic_bytes"]))
 
 
 def parse():
@@ -40,7 +63,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-cols", type=int, default=0, help="oracle sample: input columns (0 = Nm/5)")
     ap.add_argument("--no-check", action="store_true", help="skip the spot-step check against the oracle")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 3 times (reference for the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain device-to-device copy of known size: its FETCH_SIZE and
+    WRITE_SIZE readings calibrate the counters taken on the kernels."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_copy": n * 4, "copies": 3}), flush=True)
 
 
 def elem(mask, direction, s1, s2, cplx):
@@ -94,6 +133,9 @@ def cpu_baseline(shape, mask, F, m, d, cols):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
@@ -221,7 +263,8 @@ def main():
         "kernels": kernel,
         "roofline": {"bound": "hbm", "kernel": "sbgemv_n (stage 3, F)", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(Nm, Nd, Nt, mask),
+                     "algorithmic_bytes": kn["bytes"]},
         "cpu_baseline": cpu,
         "check": check,
         "context": {"page_mi355x_f_apply_ms": {"fp64": 1.9, "mixed": 1.3}},

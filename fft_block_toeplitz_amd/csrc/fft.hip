@@ -267,6 +267,19 @@ __device__ __forceinline__ void store_elem(E *base, int64_t index, E v) {
     base[index] = v;
 }
 
+__device__ __forceinline__ void store_stream(cx<float> *p, cx<float> v) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(f32x2{v.re, v.im}, reinterpret_cast<f32x2 *>(p));
+}
+__device__ __forceinline__ void store_stream2(cx<float> *p, cx<float> v0, cx<float> v1) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(f32x4{v0.re, v0.im, v1.re, v1.im}, reinterpret_cast<f32x4 *>(p));
+}
+__device__ __forceinline__ void store_stream(cx<double> *p, cx<double> v) {
+  typedef double f64x2 __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(f64x2{v.re, v.im}, reinterpret_cast<f64x2 *>(p));
+}
+
 template <typename T, typename Src, bool ROUND>
 __device__ __forceinline__ T to_compute(Src v) {
   if constexpr (ROUND && sizeof(Src) == 8) return static_cast<T>(round_f32(v));
@@ -305,20 +318,54 @@ __global__ __launch_bounds__(kBlock) void rfft_forward_kernel(FftGeom g, FwdFftA
   __syncthreads();
   middle_passes<T, -1, VMAX>(lds, g, 1, g.npass, logC, tw);
 
-  if (!live) return;
-  const int64_t row = ch / a.cpr, col = ch - row * a.cpr;
-  cx<float> *d32 = a.dst32 ? static_cast<cx<float> *>(a.dst32) + row * a.ldr32 + col : nullptr;
-  cx<double> *d64 = a.dst64 ? static_cast<cx<double> *>(a.dst64) + row * a.ldr64 + col : nullptr;
-  for (int b = threadIdx.x; b < ((L + 1) << logC); b += kBlock) {
-    int k = b >> logC;
-    int ka = k == L ? 0 : k, kb = k == 0 ? 0 : L - k;
-    cx<T> za = lds[(ka << logC) + c], zb = conj(lds[(kb << logC) + c]);
-    cx<T> e = scale(za + zb, T(0.5));
-    cx<T> dd = za - zb;
-    cx<T> o = mk(dd.im * T(0.5), -dd.re * T(0.5));  // (za - zb) / 2i
-    cx<T> x = e + cmul(o, tw[k]);
-    if (d64) d64[k * a.fstride64] = cvt<double>(x);
-    if (d32) d32[k * a.fstride32] = cvt<float>(x);
+  // X[k] for k = 0..L; each thread takes two adjacent channels of one bin so
+  // that the complex64 output goes out as 16-byte stores
+  const int half = C > 1 ? C / 2 : 1;
+  const int logh = C > 1 ? logC - 1 : 0;
+  const int cp = threadIdx.x & (half - 1);
+  const int c0 = C > 1 ? 2 * cp : 0;
+  const int nc = C > 1 ? 2 : 1;
+  const int64_t ch0 = xcd_contiguous_block(blockIdx.x, nblocks) * C + c0;
+  if (ch0 >= a.nchan) return;
+  const bool two = nc == 2 && ch0 + 1 < a.nchan;
+  const int64_t row0 = ch0 / a.cpr, col0 = ch0 - row0 * a.cpr;
+  const int64_t row1 = two ? (ch0 + 1) / a.cpr : row0, col1 = two ? ch0 + 1 - row1 * a.cpr : col0;
+  cx<float> *d32a = a.dst32 ? static_cast<cx<float> *>(a.dst32) + row0 * a.ldr32 + col0 : nullptr;
+  cx<float> *d32b = a.dst32 ? static_cast<cx<float> *>(a.dst32) + row1 * a.ldr32 + col1 : nullptr;
+  cx<double> *d64a = a.dst64 ? static_cast<cx<double> *>(a.dst64) + row0 * a.ldr64 + col0 : nullptr;
+  cx<double> *d64b = a.dst64 ? static_cast<cx<double> *>(a.dst64) + row1 * a.ldr64 + col1 : nullptr;
+  // one 16-byte store when both outputs are adjacent and 16-byte aligned
+  // (frequency strides are even)
+  const bool pack32 = two && d32b == d32a + 1 && (reinterpret_cast<uintptr_t>(d32a) & 15) == 0 &&
+                      (a.fstride32 & 1) == 0;
+  for (int b = threadIdx.x; b < ((L + 1) << logh); b += kBlock) {
+    const int k = b >> logh;
+    const int ka = k == L ? 0 : k, kb = k == 0 ? 0 : L - k;
+    const cx<T> w = tw[k];
+    cx<T> x[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (e == 1 && !two) break;
+      cx<T> za = lds[(ka << logC) + c0 + e], zb = conj(lds[(kb << logC) + c0 + e]);
+      cx<T> ev = scale(za + zb, T(0.5));
+      cx<T> dd = za - zb;
+      cx<T> o = mk(dd.im * T(0.5), -dd.re * T(0.5));  // (za - zb) / 2i
+      x[e] = ev + cmul(o, w);
+    }
+    // non-temporal: the spectrum is consumed by the next kernel, not by this
+    // one; streaming it out keeps it from lingering dirty in the caches
+    if (d64a) {
+      store_stream(d64a + k * a.fstride64, cvt<double>(x[0]));
+      if (two) store_stream(d64b + k * a.fstride64, cvt<double>(x[1]));
+    }
+    if (d32a) {
+      if (pack32) {
+        store_stream2(d32a + k * a.fstride32, cvt<float>(x[0]), cvt<float>(x[1]));
+      } else {
+        store_stream(d32a + k * a.fstride32, cvt<float>(x[0]));
+        if (two) store_stream(d32b + k * a.fstride32, cvt<float>(x[1]));
+      }
+    }
   }
 }
 
