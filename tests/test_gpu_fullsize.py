@@ -1,0 +1,115 @@
+"""GPU parity at full sizes, in the launch configuration bench.py times.
+
+Main (Nm=5000, Nd=100, Nt=1000; the single-GPU workload of "Mixed-precision
+FFTMatvec performance optimization on AMD GPUs", section 4.1) and the Scale
+share (Nm=20000, Nd=100, Nt=2000). The oracle computes sampled outputs one
+time step at a time from the definition (direct double sum); properties that
+hold at any size (adjoint identity, bitwise repeatability) cover the rest.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from fft_block_toeplitz_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def fm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fft_block_toeplitz_amd as fm
+
+    fm.lib()
+    return fm
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+class Full:
+    def __init__(self, shape):
+        self.shape = shape
+        note(f"generating {shape.name} Nm={shape.Nm} Nd={shape.Nd} Nt={shape.Nt}")
+        self.F, self.m, self.d = W.problem(shape)
+        self.F_dev = torch.from_numpy(self.F).to("cuda")
+        self.m_dev = torch.from_numpy(self.m).to("cuda")
+        self.d_dev = torch.from_numpy(self.d).to("cuda")
+        Nt = shape.Nt
+        self.fsteps = np.array([0, 1, 7, Nt // 2, Nt - 1])
+        self.asteps = np.array([0, Nt // 2, Nt - 8, Nt - 2, Nt - 1])
+        note("oracle direct sums at spot steps")
+        self.v_ref = oracle.direct(self.F, self.m, self.fsteps)
+        self.w_ref = oracle.direct_adjoint(self.F, self.d, self.asteps)
+
+    def release(self):
+        del self.F_dev
+        torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def main_case(fm):
+    c = Full(W.MAIN)
+    yield c
+    c.release()
+
+
+def check(fm, c, mask, tol, flags=0, repeat=False):
+    plan = fm.Plan(c.F_dev, mask | flags)
+    v = host(plan.apply(c.m_dev))
+    w = host(plan.apply_adjoint(c.d_dev))
+    ev = oracle.rel_l2(v[c.fsteps], c.v_ref)
+    ew = oracle.rel_l2(w[c.asteps], c.w_ref)
+    ident = abs(np.vdot(v, c.d) - np.vdot(c.m, w)) / (np.linalg.norm(v) * np.linalg.norm(c.d))
+    note(f"{c.shape.name} mask={mask:#05x} flags={flags:#x}: spot rel err F {ev:.3e} F* {ew:.3e}, "
+         f"adjoint identity {ident:.2e}")
+    assert np.isfinite(v).all() and np.isfinite(w).all()
+    assert ev <= tol and ew <= tol
+    assert ident <= tol
+    if repeat:
+        assert np.array_equal(v, host(plan.apply(c.m_dev)))
+        assert np.array_equal(w, host(plan.apply_adjoint(c.d_dev)))
+    plan.close()
+
+
+def test_main_mixed_as_benchmarked(fm, main_case):
+    check(fm, main_case, fm.FFTMV_MIXED, 1e-6, repeat=True)
+
+
+def test_main_fp64(fm, main_case):
+    check(fm, main_case, fm.FFTMV_ALL_FP64, 1e-11)
+
+
+def test_main_mixed_five_kernel_form(fm, main_case):
+    check(fm, main_case, fm.FFTMV_MIXED, 1e-6, flags=fm.FFTMV_FLAG_STAGED)
+
+
+def test_main_page_masks_separately(fm, main_case):
+    """The page's two optimal configurations, each with the other direction
+    in FP64 (F̂ held in both precisions)."""
+    check(fm, main_case, fm.FFTMV_MIXED_F, 1e-6, flags=fm.FFTMV_FLAG_FHAT_BOTH)
+    check(fm, main_case, fm.FFTMV_MIXED_FADJ, 1e-6, flags=fm.FFTMV_FLAG_FHAT_BOTH)
+
+
+@pytest.mark.slow
+def test_scale_share_mixed(fm):
+    """One GPU's share of a large grid: Nm=20000, Nd=100, Nt=2000, F̂ ~32 GB
+    in complex64."""
+    if torch.cuda.get_device_properties(0).total_memory < 80 << 30:
+        pytest.skip("needs ~70 GB of device memory")
+    c = Full(W.SCALE)
+    try:
+        check(fm, c, fm.FFTMV_MIXED, 1e-6)
+    finally:
+        c.release()
