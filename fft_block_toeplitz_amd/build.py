@@ -9,9 +9,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfftmv.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("fft.hip", "sbgemv.hip", "padcast.hip", "plan.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f)
+           for f in ("fft.hip", "fft_fixed.hip", "sbgemv.hip", "padcast.hip", "plan.cpp")]
 HEADERS = [os.path.join(ROOT, "include", "fftmv.h")] + [
-    os.path.join(HERE, "csrc", f) for f in ("common.hpp", "internal.hpp")]
+    os.path.join(HERE, "csrc", f) for f in ("common.hpp", "internal.hpp", "fft_device.hpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -23,16 +24,35 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into fft_block_toeplitz_amd/libfftmv.so."""
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, "-shared", f"-I{os.path.join(ROOT, 'include')}", *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    """Compile every HIP source (in parallel) and link
+    fft_block_toeplitz_amd/libfftmv.so."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
     noise = "packed-fp32-ops"  # the host pass does not know this device feature
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln and ln.strip()]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    inc = f"-I{os.path.join(ROOT, 'include')}"
+    with tempfile.TemporaryDirectory(prefix="fftmv_build_") as tmpdir:
+        def compile_one(src):
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cmd = [HIPCC, *FLAGS, inc, "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+        workers = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(workers) as ex:
+            results = list(ex.map(compile_one, SOURCES))
+        msgs = []
+        for (obj, res), src in zip(results, SOURCES):
+            out = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln and ln.strip()]
+            if res.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(out))
+            msgs += out
+        tmp = LIB + f".tmp{os.getpid()}"
+        cmd = [HIPCC, *FLAGS, "-shared", *[o for o, _ in results], "-o", tmp]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
     os.replace(tmp, LIB)

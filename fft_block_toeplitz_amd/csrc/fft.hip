@@ -24,97 +24,16 @@
 // stores straight to global memory, so the data cross LDS only between
 // passes. Channel tiles are numbered XCD-contiguously so that neighbouring
 // tiles, which share cache lines, share an L2.
-#include "common.hpp"
-#include "internal.hpp"
+#include "fft_device.hpp"
 
 namespace fftmv {
 namespace {
 
-// A thread keeps at most VMAX complex values in registers during a pass,
-// i.e. VMAX / R butterflies of radix R; the host picks C (channels per
-// workgroup) and VMAX so that every pass of the schedule fits.
-constexpr int kVmaxSmall = 20;
-constexpr int kVmaxLarge = 40;
-
-// ---------------------------------------------------------------- DFTs
-// y_q = sum_p x_p exp(S 2 pi i p q / R), in place, S = -1 forward, +1 inverse.
-template <int S, typename T>
-__device__ __forceinline__ void dft2(cx<T> &a, cx<T> &b) {
-  cx<T> t = a - b;
-  a = a + b;
-  b = t;
-}
-
-template <int S, typename T>
-__device__ __forceinline__ void dft4(cx<T> &x0, cx<T> &x1, cx<T> &x2, cx<T> &x3) {
-  cx<T> t0 = x0 + x2, t1 = x0 - x2, t2 = x1 + x3, t3 = mul_si<S>(x1 - x3);
-  x0 = t0 + t2;
-  x2 = t0 - t2;
-  x1 = t1 + t3;
-  x3 = t1 - t3;
-}
-
-template <int S, typename T>
-__device__ __forceinline__ void dft8(cx<T> *x) {
-  // two length-4 transforms of the even and odd samples, then the
-  // exp(S 2 pi i q / 8) twiddles and one radix-2 step
-  const T h = T(0.70710678118654752440084436210484903928);  // 1/sqrt(2)
-  dft4<S>(x[0], x[2], x[4], x[6]);
-  dft4<S>(x[1], x[3], x[5], x[7]);
-  cx<T> b1 = x[3], b2 = x[5], b3 = x[7];
-  // positions: even transform a_q at x[0],x[2],x[4],x[6]; odd b_q at x[1],x[3],x[5],x[7]
-  cx<T> a0 = x[0], a1 = x[2], a2 = x[4], a3 = x[6], b0 = x[1];
-  b1 = mk((b1.re - S * b1.im) * h, (b1.im + S * b1.re) * h);   // * (1 + S i)/sqrt 2
-  b2 = mul_si<S>(b2);                                          // * S i
-  b3 = mk((-b3.re - S * b3.im) * h, (S * b3.re - b3.im) * h);  // * (-1 + S i)/sqrt 2
-  x[0] = a0 + b0;
-  x[4] = a0 - b0;
-  x[1] = a1 + b1;
-  x[5] = a1 - b1;
-  x[2] = a2 + b2;
-  x[6] = a2 - b2;
-  x[3] = a3 + b3;
-  x[7] = a3 - b3;
-}
-
-template <int S, typename T>
-__device__ __forceinline__ void dft5(cx<T> *x) {
-  // cos and sin of 2 pi / 5 and 4 pi / 5
-  const T c1 = T(0.30901699437494742410229341718281905886);
-  const T c2 = T(-0.80901699437494742410229341718281905886);
-  const T s1 = T(0.95105651629515357211643933337938214340);
-  const T s2 = T(0.58778525229247312916870595463907276860);
-  cx<T> t1 = x[1] + x[4], t2 = x[2] + x[3], t3 = x[1] - x[4], t4 = x[2] - x[3];
-  cx<T> a1 = mk(x[0].re + c1 * t1.re + c2 * t2.re, x[0].im + c1 * t1.im + c2 * t2.im);
-  cx<T> a2 = mk(x[0].re + c2 * t1.re + c1 * t2.re, x[0].im + c2 * t1.im + c1 * t2.im);
-  cx<T> b1 = mk(s1 * t3.re + s2 * t4.re, s1 * t3.im + s2 * t4.im);
-  cx<T> b2 = mk(s2 * t3.re - s1 * t4.re, s2 * t3.im - s1 * t4.im);
-  x[0] = x[0] + t1 + t2;
-  b1 = mul_si<S>(b1);
-  b2 = mul_si<S>(b2);
-  x[1] = a1 + b1;
-  x[4] = a1 - b1;
-  x[2] = a2 + b2;
-  x[3] = a2 - b2;
-}
-
-template <int R, int S, typename T>
-__device__ __forceinline__ void dft(cx<T> *x) {
-  if constexpr (R == 2) dft2<S>(x[0], x[1]);
-  else if constexpr (R == 4) dft4<S>(x[0], x[1], x[2], x[3]);
-  else if constexpr (R == 5) dft5<S>(x);
-  else dft8<S>(x);
-}
-
-template <typename T, int R, int S>
-__device__ __forceinline__ void twiddle(cx<T> *v, int k, int twstep, const cx<T> *__restrict__ tw) {
-#pragma unroll
-  for (int q = 1; q < R; ++q) {
-    cx<T> w = tw[k * q * twstep];
-    v[q] = S < 0 ? cmul(v[q], w) : cmulc(v[q], w);
-  }
-}
-
+// A thread keeps at most kVmax complex values in registers during a pass,
+// i.e. kVmax / R butterflies of radix R; the host picks C (channels per
+// workgroup) so that every pass of the schedule fits. With C = 1 every
+// supported length (Nt <= 4096) fits.
+constexpr int kVmax = 20;
 // One Stockham pass of radix R over the [L][C] LDS tile. Butterfly j of
 // channel c reads elements j + q L/R, multiplies input q by
 // w_{Ns R}^{(j mod Ns) q} and writes output q to (j - j mod Ns) R + j mod Ns + q Ns.
@@ -246,40 +165,6 @@ __device__ __forceinline__ void last_pass_any(int R, const cx<T> *lds, int L, in
     default: last_pass<T, 8, S, VMAX>(lds, L, logC, twstep, tw, put); break;
   }
 }
-
-// Element at base + index. OFF32: the index fits 32 bits in bytes, so the
-// address is a uniform base plus one 32-bit per-lane offset (one VGPR per
-// load in flight instead of a 64-bit address pair).
-template <bool OFF32, typename E>
-__device__ __forceinline__ E load_elem(const E *base, int64_t index) {
-  if constexpr (OFF32)
-    return *reinterpret_cast<const E *>(reinterpret_cast<const char *>(base) +
-                                        static_cast<uint32_t>(index) * static_cast<uint32_t>(sizeof(E)));
-  else
-    return base[index];
-}
-template <bool OFF32, typename E>
-__device__ __forceinline__ void store_elem(E *base, int64_t index, E v) {
-  if constexpr (OFF32)
-    *reinterpret_cast<E *>(reinterpret_cast<char *>(base) +
-                           static_cast<uint32_t>(index) * static_cast<uint32_t>(sizeof(E))) = v;
-  else
-    base[index] = v;
-}
-
-__device__ __forceinline__ void store_stream(cx<float> *p, cx<float> v) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  __builtin_nontemporal_store(f32x2{v.re, v.im}, reinterpret_cast<f32x2 *>(p));
-}
-__device__ __forceinline__ void store_stream2(cx<float> *p, cx<float> v0, cx<float> v1) {
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
-  __builtin_nontemporal_store(f32x4{v0.re, v0.im, v1.re, v1.im}, reinterpret_cast<f32x4 *>(p));
-}
-__device__ __forceinline__ void store_stream(cx<double> *p, cx<double> v) {
-  typedef double f64x2 __attribute__((ext_vector_type(2)));
-  __builtin_nontemporal_store(f64x2{v.re, v.im}, reinterpret_cast<f64x2 *>(p));
-}
-
 template <typename T, typename Src, bool ROUND>
 __device__ __forceinline__ T to_compute(Src v) {
   if constexpr (ROUND && sizeof(Src) == 8) return static_cast<T>(round_f32(v));
@@ -437,35 +322,26 @@ __global__ __launch_bounds__(kBlock) void rfft_inverse_kernel(FftGeom g, InvFftA
   const int pl = g.npass - 1;
   last_pass_any<T, +1, VMAX>(g.radix[pl], lds, L, logC, g.twstep[pl], tw, put);
 }
-
-int ilog2(int c) {
-  int l = 0;
-  while ((1 << l) < c) ++l;
-  return l;
-}
-
 }  // namespace
 
-// (channels per workgroup, VMAX) for a schedule, precision and batch: the
-// widest C that still gives at least 1024 workgroups (four per CU), with the
-// smaller register budget when it fits; for small batches the narrowest C
-// (most workgroups). C = 0 when the transform does not fit at all.
+// Channels per workgroup for a schedule, precision and batch: the widest C
+// that still gives at least 1024 workgroups (four per CU); for small batches
+// the narrowest C (most workgroups). C = 0 when the transform does not fit.
 FftLaunch fft_launch_config(const FftGeom &g, bool f32, int64_t nchan) {
   const int64_t esz = f32 ? 8 : 16;
-  auto fits = [&](int C, int vmax) {
+  auto fits = [&](int C) {
     if (static_cast<int64_t>(g.L) * C * esz > kMaxLds) return false;
     for (int p = 0; p < g.npass; ++p) {
       const int64_t nb = static_cast<int64_t>(g.L / g.radix[p]) * C;
-      if (nb > static_cast<int64_t>(vmax / g.radix[p]) * kBlock) return false;
+      if (nb > static_cast<int64_t>(kVmax / g.radix[p]) * kBlock) return false;
     }
     return true;
   };
   FftLaunch narrowest;
   for (int C = kMaxChannelsPerBlock; C >= 1; C >>= 1) {
-    const int vmax = fits(C, kVmaxSmall) ? kVmaxSmall : fits(C, kVmaxLarge) ? kVmaxLarge : 0;
-    if (vmax == 0) continue;
-    if ((nchan + C - 1) / C >= 1024) return {C, vmax};
-    narrowest = {C, vmax};
+    if (!fits(C)) continue;
+    if ((nchan + C - 1) / C >= 1024) return {C, kVmax};
+    narrowest = {C, kVmax};
   }
   return narrowest;
 }
@@ -474,58 +350,34 @@ int fft_channels_per_block(const FftGeom &g, bool f32, int64_t nchan) { return f
 
 namespace {
 
-// byte extent below 4 GiB: 32-bit offsets are exact
-bool fits_32bit(int64_t rows, int64_t ld, int64_t esz) { return rows * ld * esz < (int64_t(1) << 32); }
+
+int ilog2(int c) {
+  int l = 0;
+  while ((1 << l) < c) ++l;
+  return l;
+}
 
 template <typename T, typename Src, bool ROUND>
 void fwd(const FftGeom &g, const FwdFftArgs &a, const FftLaunch &cfg, const void *tw, hipStream_t s) {
   const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
   const size_t lds = static_cast<size_t>(g.L) * cfg.C * sizeof(cx<T>);
-  auto twp = static_cast<const cx<T> *>(tw);
-  const int logC = ilog2(cfg.C);
-  const dim3 grid(static_cast<unsigned>(nblocks));
-  const bool off32 = fits_32bit(a.Nt, a.src_ld, sizeof(Src));
-  if (cfg.vmax == kVmaxSmall && off32)
-    hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmaxSmall, true>), grid, dim3(kBlock), lds, s, g, a,
-                       logC, twp, nblocks);
-  else if (cfg.vmax == kVmaxSmall)
-    hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmaxSmall, false>), grid, dim3(kBlock), lds, s, g, a,
-                       logC, twp, nblocks);
-  else if (off32)
-    hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmaxLarge, true>), grid, dim3(kBlock), lds, s, g, a,
-                       logC, twp, nblocks);
-  else
-    hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmaxLarge, false>), grid, dim3(kBlock), lds, s, g, a,
-                       logC, twp, nblocks);
+  hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmax, false>), dim3(static_cast<unsigned>(nblocks)),
+                     dim3(kBlock), lds, s, g, a, ilog2(cfg.C), static_cast<const cx<T> *>(tw), nblocks);
 }
 
 template <typename T, typename Src>
 void inv(const FftGeom &g, const InvFftArgs &a, const FftLaunch &cfg, const void *tw, hipStream_t s) {
   const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
   const size_t lds = static_cast<size_t>(g.L) * cfg.C * sizeof(cx<T>);
-  auto twp = static_cast<const cx<T> *>(tw);
-  const T inv_l = T(1) / static_cast<T>(g.L);
-  const int logC = ilog2(cfg.C);
-  const dim3 grid(static_cast<unsigned>(nblocks));
-  const bool off32 = fits_32bit(g.L + 1, a.src_ld, sizeof(cx<Src>)) && fits_32bit(a.Nt, a.dst_ld, 8);
-  if (cfg.vmax == kVmaxSmall && off32)
-    hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmaxSmall, true>), grid, dim3(kBlock), lds, s, g, a, logC, twp,
-                       inv_l, nblocks);
-  else if (cfg.vmax == kVmaxSmall)
-    hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmaxSmall, false>), grid, dim3(kBlock), lds, s, g, a, logC,
-                       twp, inv_l, nblocks);
-  else if (off32)
-    hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmaxLarge, true>), grid, dim3(kBlock), lds, s, g, a, logC, twp,
-                       inv_l, nblocks);
-  else
-    hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmaxLarge, false>), grid, dim3(kBlock), lds, s, g, a, logC,
-                       twp, inv_l, nblocks);
+  hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmax, false>), dim3(static_cast<unsigned>(nblocks)), dim3(kBlock),
+                     lds, s, g, a, ilog2(cfg.C), static_cast<const cx<T> *>(tw), T(1) / static_cast<T>(g.L),
+                     nblocks);
 }
 
 }  // namespace
-
 hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s) {
+  if (launch_fft_forward_fixed(g, a, compute_f32, tw, s)) return hipGetLastError();
   const FftLaunch cfg = fft_launch_config(g, compute_f32, a.nchan);
   if (cfg.C == 0 || (a.nchan + cfg.C - 1) / cfg.C > INT32_MAX) return hipErrorInvalidValue;
   if (compute_f32) {
@@ -543,9 +395,9 @@ hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool comput
   }
   return hipGetLastError();
 }
-
 hipError_t launch_fft_inverse(const FftGeom &g, const InvFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s) {
+  if (launch_fft_inverse_fixed(g, a, compute_f32, tw, s)) return hipGetLastError();
   const FftLaunch cfg = fft_launch_config(g, compute_f32, a.nchan);
   if (cfg.C == 0 || (a.nchan + cfg.C - 1) / cfg.C > INT32_MAX) return hipErrorInvalidValue;
   if (compute_f32) {
@@ -561,5 +413,4 @@ hipError_t launch_fft_inverse(const FftGeom &g, const InvFftArgs &a, bool comput
   }
   return hipGetLastError();
 }
-
 }  // namespace fftmv

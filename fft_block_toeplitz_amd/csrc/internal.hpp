@@ -13,12 +13,49 @@ constexpr int kMaxChannelsPerBlock = 32;
 // Stockham radix schedule of the length-L complex FFT that carries the
 // length-2L real FFT (even samples in the real part, odd in the imaginary).
 struct FftGeom {
-  int L = 0;        // complex length (= Nt)
+  int L = 0;        // complex length (= Nt); 0 = unsupported length
   int npass = 0;
   int radix[kMaxPasses] = {};
   int ns[kMaxPasses] = {};      // product of the radices before this pass
   int twstep[kMaxPasses] = {};  // 2L / (ns * radix): exponent step in the w_{2L} table
 };
+
+// Radix schedule for L = 2^a 5^b: radix 8 while more than four factors of
+// two remain, then 4 4 / 8 / 4 / 2, then the fives. Usable on the host and,
+// as a constant expression, in kernels specialised for one length.
+constexpr FftGeom make_geometry(int L) {
+  FftGeom g{};
+  if (L < 1) return g;
+  int r = L, a = 0, b = 0;
+  while (r % 2 == 0) r /= 2, ++a;
+  while (r % 5 == 0) r /= 5, ++b;
+  if (r != 1) return g;
+  int np = 0;
+  while (a > 4) {
+    g.radix[np++] = 8;
+    a -= 3;
+  }
+  if (a == 4) {
+    g.radix[np++] = 4;
+    g.radix[np++] = 4;
+  } else if (a == 3) {
+    g.radix[np++] = 8;
+  } else if (a == 2) {
+    g.radix[np++] = 4;
+  } else if (a == 1) {
+    g.radix[np++] = 2;
+  }
+  for (int i = 0; i < b; ++i) g.radix[np++] = 5;
+  g.L = L;
+  g.npass = np;
+  int ns = 1;
+  for (int p = 0; p < np; ++p) {
+    g.ns[p] = ns;
+    g.twstep[p] = 2 * L / (ns * g.radix[p]);
+    ns *= g.radix[p];
+  }
+  return g;
+}
 
 // Batched forward real FFT: nchan channels of Nt real samples (implicitly
 // zero-padded to 2 Nt), channel ch at src[t * src_ld + ch]; writes the Nt+1
@@ -86,6 +123,12 @@ int fft_channels_per_block(const FftGeom &g, bool f32, int64_t nchan);
 hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s);
 hipError_t launch_fft_inverse(const FftGeom &g, const InvFftArgs &a, bool compute_f32, const void *tw,
+                              hipStream_t s);
+// Fixed-length kernels (fft_fixed.hip): launch and return true when one
+// covers this transform, else return false and launch nothing.
+bool launch_fft_forward_fixed(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
+                              hipStream_t s);
+bool launch_fft_inverse_fixed(const FftGeom &g, const InvFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s);
 hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s);
 hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s);

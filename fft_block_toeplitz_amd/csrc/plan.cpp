@@ -62,44 +62,11 @@ int status_from_hip(hipError_t e) {
     if (e_ != hipSuccess) return status_from_hip(e_); \
   } while (0)
 
-// Radix schedule for the length-L complex FFT, L = 2^a 5^b. Radix 8 while
-// more than four factors of two remain, then 4 4 / 8 / 4 / 2, then the 5s.
 bool build_geometry(int64_t L, FftGeom *g) {
-  int64_t r = L;
-  int a = 0, b = 0;
-  while (r % 2 == 0) r /= 2, ++a;
-  while (r % 5 == 0) r /= 5, ++b;
-  if (r != 1) return false;
-  int np = 0;
-  auto push = [&](int R) {
-    if (np >= kMaxPasses) return false;
-    g->radix[np++] = R;
-    return true;
-  };
-  while (a > 4) {
-    if (!push(8)) return false;
-    a -= 3;
-  }
-  if (a == 4) {
-    if (!push(4) || !push(4)) return false;
-  } else if (a == 3) {
-    if (!push(8)) return false;
-  } else if (a == 2) {
-    if (!push(4)) return false;
-  } else if (a == 1) {
-    if (!push(2)) return false;
-  }
-  for (int i = 0; i < b; ++i)
-    if (!push(5)) return false;
-  g->L = static_cast<int>(L);
-  g->npass = np;
-  int ns = 1;
-  for (int p = 0; p < np; ++p) {
-    g->ns[p] = ns;
-    g->twstep[p] = static_cast<int>((2 * L) / (static_cast<int64_t>(ns) * g->radix[p]));
-    ns *= g->radix[p];
-  }
-  return true;
+  // lengths with more than kMaxPasses passes are far above the LDS limit
+  if (L < 1 || L > (int64_t(1) << 20)) return false;
+  *g = make_geometry(static_cast<int>(L));
+  return g->L == L;
 }
 
 // exp(-2 pi i t / N) with the angle reduced exactly in integers to
