@@ -88,6 +88,9 @@ SHAPES = [
     (1001, 3, 8),
     (2, 130, 40),    # Nd > Nm: tall blocks
     (129, 65, 1000), # Main's time length, ragged channel counts
+    (33, 7, 2000),   # the Scale share's time length, narrow batches
+    (3, 2, 4096),    # the longest supported transform, 2Nt = 2^13
+    (2, 3, 3125),    # 2Nt = 2 * 5^5
 ]
 
 
@@ -168,10 +171,11 @@ def test_stage_by_stage(fm, mask):
     plan.close()
 
 
-def test_all_precision_masks(fm):
+@pytest.mark.parametrize("shape", [(37, 5, 20), (37, 5, 1000)])
+def test_all_precision_masks(fm, shape):
     """Every one of the 32 per-stage precision choices of each direction,
     on one plan holding Fhat in both precisions."""
-    c = case(37, 5, 20)
+    c = case(*shape)
     plan = fm.Plan(c.F_dev, fm.FFTMV_FLAG_FHAT_BOTH)
     worst = {}
     for direction in (0, 1):
