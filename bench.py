@@ -105,30 +105,60 @@ def sbgemv_bytes(Nm, Nd, Nt, mask, direction):
     return fhat + K * nin * elem(mask, direction, 2, 3, True) + K * nout * elem(mask, direction, 3, 4, True)
 
 
+def host_info():
+    """Host CPU model and the thread settings the oracle runs under."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(),
+            "sched_affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(shape, mask, F, m, d, cols):
     """The FP64 CPU oracle (as it stands) on a column sample of the same
     workload: Nm reduced to `cols`, everything else unchanged. One F and one
-    F* apply with Fhat precomputed, median of 3; scaled to the full step by
-    the byte model."""
+    F* apply with Fhat precomputed, median of 3, on all the threads the
+    oracle uses and again on one thread; scaled to the full step by the byte
+    model."""
     import oracle
 
     Nm, Nd, Nt = shape.Nm, shape.Nd, shape.Nt
     Fs = np.ascontiguousarray(F[:, :, :cols])
     ms = np.ascontiguousarray(m[:, :cols])
     Fh = oracle.setup(Fs)
-    times = []
-    for _ in range(3):
-        t0 = time.perf_counter()
-        oracle.apply(Fh, ms)
-        oracle.apply_adjoint(Fh, d)
-        times.append(time.perf_counter() - t0)
-    t = float(np.median(times))
     sample_bytes = apply_bytes(cols, Nd, Nt, mask, 0) + apply_bytes(cols, Nd, Nt, mask, 1)
+
+    def timed(reps):
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.apply(Fh, ms)
+            oracle.apply_adjoint(Fh, d)
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times))
+
+    threads = oracle.num_threads()
+    t = timed(3)
+    oracle.set_num_threads(1)
+    try:
+        t1 = timed(1)
+    finally:
+        oracle.set_num_threads(threads)
     gbs = sample_bytes / t / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"F and F* apply at Nm={cols} (of {Nm}), Nd={Nd}, Nt={Nt}, FP64 oracle, Fhat precomputed, "
                       f"median of 3: {t * 1e3:.1f} ms; GB/s on the step's byte model at that Nm",
-            "ms_per_step_full_equiv": round(t * 1e3 * Nm / cols, 1)}
+            "ms_per_step_full_equiv": round(t * 1e3 * Nm / cols, 1),
+            "one_thread": {"value": round(sample_bytes / t1 / 1e9, 3), "unit": "GB/s",
+                           "ms_per_step_full_equiv": round(t1 * 1e3 * Nm / cols, 1)},
+            "host": host_info()}
 
 
 def main():
@@ -257,6 +287,8 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 1),
         "f_apply_ms": round(fmed, 4),
         "fadj_apply_ms": round(amed, 4),
+        "f_apply_ms_min": round(float(np.min(f_ms)), 4),
+        "fadj_apply_ms_min": round(float(np.min(a_ms)), 4),
         "f_apply_GBs": round(bF / (fmed * 1e-3) / 1e9, 1),
         "fadj_apply_GBs": round(bA / (amed * 1e-3) / 1e9, 1),
         "bytes_per_step": bF + bA,
