@@ -29,6 +29,7 @@ FFTMV_ERR_UNSUPPORTED_SIZE = -2
 FFTMV_ERR_OUT_OF_MEMORY = -3
 FFTMV_ERR_HIP = -4
 FFTMV_ERR_INTERNAL = -5
+FFTMV_ERR_NO_CONFIG = -6
 
 FFTMV_DIR_F = 0
 FFTMV_DIR_FADJ = 1
@@ -39,9 +40,11 @@ FFTMV_MIXED = 0x186
 FFTMV_PREC_BITS = 0x3FF
 FFTMV_FLAG_STAGED = 1 << 16
 FFTMV_FLAG_FHAT_BOTH = 1 << 17
+FFTMV_MODEL_PARAMS = 9
 
 EXPORTS = ("fftmv_setup", "fftmv_apply", "fftmv_apply_adjoint", "fftmv_destroy", "fftmv_status_string",
-           "fftmv_query", "fftmv_set_mask", "fftmv_run_stages", "fftmv_buffer", "fftmv_version")
+           "fftmv_query", "fftmv_set_mask", "fftmv_run_stages", "fftmv_buffer", "fftmv_model_defaults",
+           "fftmv_predict", "fftmv_pareto_front", "fftmv_select_precision", "fftmv_condition", "fftmv_version")
 
 
 def FFTMV_FP32(direction: int, stage: int) -> int:
@@ -89,6 +92,12 @@ def lib() -> ctypes.CDLL:
     L.fftmv_set_mask.argtypes = [P, U32]
     L.fftmv_run_stages.argtypes = [P, I, I, I, P, P, P]
     L.fftmv_buffer.argtypes = [P, I, ctypes.POINTER(P), ctypes.POINTER(I64), ctypes.POINTER(I)]
+    D, DP = ctypes.c_double, ctypes.POINTER(ctypes.c_double)
+    L.fftmv_model_defaults.argtypes = [I, DP]
+    L.fftmv_predict.argtypes = [I64, I64, I64, I, U32, U32, D, DP, DP, DP]
+    L.fftmv_pareto_front.argtypes = [I64, I64, I64, I, U32, D, D, DP, ctypes.POINTER(U32), ctypes.POINTER(I)]
+    L.fftmv_select_precision.argtypes = [I64, I64, I64, I, U32, D, D, DP, ctypes.POINTER(U32), DP, DP]
+    L.fftmv_condition.argtypes = [P, I, DP, DP, DP, P]
     L.fftmv_version.argtypes = []
     for name in EXPORTS:
         if name != "fftmv_status_string":
@@ -144,6 +153,62 @@ def fftmv_buffer(plan: int, which: int) -> tuple[int, int, int]:
     p, ld, eb = ctypes.c_void_p(), ctypes.c_int64(), ctypes.c_int()
     _check(lib().fftmv_buffer(plan, which, ctypes.byref(p), ctypes.byref(ld), ctypes.byref(eb)), "fftmv_buffer")
     return p.value or 0, ld.value, eb.value
+
+
+def _params(params):
+    if params is None:
+        return None
+    vals = [float(x) for x in params]
+    if len(vals) != FFTMV_MODEL_PARAMS:
+        raise ValueError(f"model parameters: expected {FFTMV_MODEL_PARAMS} values, got {len(vals)}")
+    return (ctypes.c_double * FFTMV_MODEL_PARAMS)(*vals)
+
+
+def fftmv_model_defaults(direction: int) -> list[float]:
+    """[c1, c2, c3, c4, c5, cF, HBM bytes/s, LDS bytes/s, seconds per kernel]."""
+    out = (ctypes.c_double * FFTMV_MODEL_PARAMS)()
+    _check(lib().fftmv_model_defaults(direction, out), "fftmv_model_defaults")
+    return list(out)
+
+
+def fftmv_predict(Nm: int, Nd: int, Nt: int, direction: int, stage_bits: int, flags: int, kappa: float,
+                  params=None) -> tuple[float, float]:
+    """(predicted relative error, predicted apply seconds) of one configuration."""
+    e, t = ctypes.c_double(), ctypes.c_double()
+    _check(lib().fftmv_predict(Nm, Nd, Nt, direction, stage_bits, flags, kappa, _params(params), ctypes.byref(e),
+                               ctypes.byref(t)), "fftmv_predict")
+    return e.value, t.value
+
+
+def fftmv_pareto_front(Nm: int, Nd: int, Nt: int, direction: int, flags: int, kappa: float, error_tol: float,
+                       params=None) -> list[int]:
+    """Stage-bit configurations on the feasible Pareto front, fastest first."""
+    front, n = (ctypes.c_uint32 * 32)(), ctypes.c_int()
+    _check(lib().fftmv_pareto_front(Nm, Nd, Nt, direction, flags, kappa, error_tol, _params(params), front,
+                                    ctypes.byref(n)), "fftmv_pareto_front")
+    return list(front[:n.value])
+
+
+def fftmv_select_precision(Nm: int, Nd: int, Nt: int, direction: int, flags: int, kappa: float,
+                           error_tol: float, params=None) -> tuple[int, float, float, bool]:
+    """(stage bits, predicted error, predicted seconds, feasible). When no
+    configuration meets the tolerance, feasible is False and the all-FP64
+    configuration is reported."""
+    b, e, t = ctypes.c_uint32(), ctypes.c_double(), ctypes.c_double()
+    st = lib().fftmv_select_precision(Nm, Nd, Nt, direction, flags, kappa, error_tol, _params(params),
+                                      ctypes.byref(b), ctypes.byref(e), ctypes.byref(t))
+    if st not in (FFTMV_SUCCESS, FFTMV_ERR_NO_CONFIG):
+        _check(st, "fftmv_select_precision")
+    return b.value, e.value, t.value, st == FFTMV_SUCCESS
+
+
+def fftmv_condition(plan: int, iters: int, K: int, stream: int = 0):
+    """(kappa, sigma_max[K], sigma_min[K]) of the plan's frequency blocks;
+    K = Nt + 1. Synchronises the stream."""
+    kappa = ctypes.c_double()
+    smax, smin = (ctypes.c_double * K)(), (ctypes.c_double * K)()
+    _check(lib().fftmv_condition(plan, iters, ctypes.byref(kappa), smax, smin, stream), "fftmv_condition")
+    return kappa.value, list(smax), list(smin)
 
 
 def fftmv_version() -> int:
@@ -205,6 +270,10 @@ class Plan:
     def run_stages(self, direction: int, first: int, last: int, x=None, out=None, stream=None) -> None:
         fftmv_run_stages(self.handle, direction, first, last, None if x is None else x.data_ptr(),
                          None if out is None else out.data_ptr(), _stream_handle(stream))
+
+    def condition(self, iters: int = 0, stream=None):
+        """(kappa, sigma_max per frequency, sigma_min per frequency) of Fhat."""
+        return fftmv_condition(self.handle, iters, self.Nt + 1, _stream_handle(stream))
 
     def query(self) -> tuple[int, int]:
         return fftmv_query(self.handle)

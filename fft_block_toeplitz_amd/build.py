@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfftmv.so")
 SOURCES = [os.path.join(HERE, "csrc", f)
-           for f in ("fft.hip", "fft_fixed.hip", "sbgemv.hip", "padcast.hip", "plan.cpp")]
+           for f in ("fft.hip", "fft_fixed.hip", "sbgemv.hip", "padcast.hip", "condition.hip", "plan.cpp",
+                     "precision.cpp")]
 HEADERS = [os.path.join(ROOT, "include", "fftmv.h")] + [
     os.path.join(HERE, "csrc", f) for f in ("common.hpp", "internal.hpp", "fft_device.hpp")]
 

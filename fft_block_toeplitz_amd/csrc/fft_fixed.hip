@@ -157,7 +157,9 @@ __device__ __forceinline__ void ct_last_pass(const cx<T> *lds, const cx<T> *__re
 
 // Forward transform of FP64 input, length L = Nt, into complex64 or
 // complex128 (apply path: one output row per frequency, 32-bit offsets).
-template <typename T, int L, int C, int TPB, bool NTS>
+// ROUND: an FP64 transform of samples first rounded to binary32 (an FP32
+// stage 1 ahead of an FP64 stage 2); FP32 transforms round on conversion.
+template <typename T, int L, int C, int TPB, bool NTS, bool ROUND>
 __global__ __launch_bounds__(TPB) void rfft_forward_ct(FwdFftArgs a, const cx<T> *__restrict__ tw,
                                                        int64_t nblocks) {
   constexpr FftGeom g = make_geometry(L);
@@ -173,8 +175,14 @@ __global__ __launch_bounds__(TPB) void rfft_forward_ct(FwdFftArgs a, const cx<T>
     const int t0 = 2 * n;  // t0 < L = Nt is guaranteed for n < NZ, L even or odd
     T re = T(0), im = T(0);
     if (live) {
-      re = static_cast<T>(load_elem<true>(src, t0 * ld + ch));
-      if (t0 + 1 < L) im = static_cast<T>(load_elem<true>(src, (t0 + 1) * ld + ch));
+      double x0 = load_elem<true>(src, t0 * ld + ch), x1 = 0.0;
+      if (t0 + 1 < L) x1 = load_elem<true>(src, (t0 + 1) * ld + ch);
+      if constexpr (ROUND) {
+        x0 = round_f32(x0);
+        x1 = round_f32(x1);
+      }
+      re = static_cast<T>(x0);
+      im = static_cast<T>(x1);
     }
     return mk(re, im);
   };
@@ -288,27 +296,37 @@ constexpr CtTile ct_wide_tile(int L) {
 constexpr bool has_ct(int L) { return L == 1000 || L == 2000; }
 constexpr int64_t kWideBatch = 4096;  // channels from which wide tiles pay
 
-template <typename T, int L, int C, int TPB = kBlock, bool NTS = true>
+template <typename T, int L, bool ROUND, int C, int TPB = kBlock>
 void launch_fwd_ct(const FwdFftArgs &a, const void *tw, hipStream_t s) {
   const int64_t nblocks = (a.nchan + C - 1) / C;
-  hipLaunchKernelGGL((rfft_forward_ct<T, L, C, TPB, NTS>), dim3(static_cast<unsigned>(nblocks)), dim3(TPB), 0, s,
-                     a, static_cast<const cx<T> *>(tw), nblocks);
+  hipLaunchKernelGGL((rfft_forward_ct<T, L, C, TPB, true, ROUND>), dim3(static_cast<unsigned>(nblocks)), dim3(TPB),
+                     0, s, a, static_cast<const cx<T> *>(tw), nblocks);
 }
 
-template <typename T, int L>
+template <typename T, int L, bool ROUND>
 void launch_fwd_ct_c(const FwdFftArgs &a, const void *tw, hipStream_t s) {
   constexpr CtTile w = ct_wide_tile<T>(L);
   if (a.nchan >= kWideBatch)
-    launch_fwd_ct<T, L, w.C, w.tpb>(a, tw, s);
+    launch_fwd_ct<T, L, ROUND, w.C, w.tpb>(a, tw, s);
   else
-    launch_fwd_ct<T, L, 1>(a, tw, s);
+    launch_fwd_ct<T, L, ROUND, 1>(a, tw, s);
+}
+
+template <int L>
+void launch_fwd_ct_any(const FwdFftArgs &a, bool compute_f32, const void *tw, hipStream_t s) {
+  if (compute_f32)
+    launch_fwd_ct_c<float, L, false>(a, tw, s);  // conversion to float rounds
+  else if (a.round_f32)
+    launch_fwd_ct_c<double, L, true>(a, tw, s);
+  else
+    launch_fwd_ct_c<double, L, false>(a, tw, s);
 }
 
 // the specialised forward kernel covers the apply path: FP64 input, one
 // output row per frequency, byte offsets below 4 GiB
 bool fwd_ct_applies(const FftGeom &g, const FwdFftArgs &a) {
-  return has_ct(g.L) && a.Nt == g.L && !a.src_f32 && !a.round_f32 && a.cpr >= a.nchan &&
-         fits_32bit(a.Nt, a.src_ld, 8) && a.nchan <= a.src_ld;
+  return has_ct(g.L) && a.Nt == g.L && !a.src_f32 && a.cpr >= a.nchan && fits_32bit(a.Nt, a.src_ld, 8) &&
+         a.nchan <= a.src_ld;
 }
 
 template <typename T, typename Src, int L, int C, int TPB = kBlock>
@@ -346,13 +364,10 @@ bool inv_ct_applies(const FftGeom &g, const InvFftArgs &a) {
 bool launch_fft_forward_fixed(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s) {
   if (!fwd_ct_applies(g, a)) return false;
-  if (compute_f32) {
-    if (g.L == 1000) launch_fwd_ct_c<float, 1000>(a, tw, s);
-    else launch_fwd_ct_c<float, 2000>(a, tw, s);
-  } else {
-    if (g.L == 1000) launch_fwd_ct_c<double, 1000>(a, tw, s);
-    else launch_fwd_ct_c<double, 2000>(a, tw, s);
-  }
+  if (g.L == 1000)
+    launch_fwd_ct_any<1000>(a, compute_f32, tw, s);
+  else
+    launch_fwd_ct_any<2000>(a, compute_f32, tw, s);
   return true;
 }
 

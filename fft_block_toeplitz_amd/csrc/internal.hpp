@@ -134,4 +134,25 @@ hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
 hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s);
 hipError_t launch_cast(const CastArgs &a, hipStream_t s);
 
+// Lanczos process on the per-frequency Gram matrices (condition.hip). One
+// frequency's vectors have n complex entries; vector j of frequency k is
+// Q + (j * K + k) * ldq (complex128).
+constexpr int kMaxLanczos = 512;
+struct LanczosArgs {
+  int64_t K = 0, n = 0;
+  double *Q = nullptr;  // basis [J+1][K][ldq] complex128
+  int64_t ldq = 0;
+  double *z = nullptr;  // G q_j on entry to a step [K][ldz] complex128
+  int64_t ldz = 0;
+  void *xin = nullptr;  // the next GEMV input [K][ldx], complex64 if x_f32
+  int64_t ldx = 0;
+  bool x_f32 = false;
+  double *alpha = nullptr, *beta = nullptr;  // [J][K]
+  int *len = nullptr;                        // [K] completed steps (negative once stopped)
+};
+hipError_t launch_lanczos_start(const LanczosArgs &a, hipStream_t s);
+hipError_t launch_lanczos_step(const LanczosArgs &a, int j, hipStream_t s);
+// sigma[2k] = largest, sigma[2k+1] = smallest singular value of block k
+hipError_t launch_lanczos_extremes(const LanczosArgs &a, double *sigma, hipStream_t s);
+
 }  // namespace fftmv

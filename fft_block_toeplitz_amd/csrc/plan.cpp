@@ -4,6 +4,7 @@
 // for the adjoint and the per-stage precision choice).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -350,6 +351,122 @@ int setup_impl(fftmv_plan_s *p, const double *F, hipStream_t s) {
   return FFTMV_SUCCESS;
 }
 
+// Device memory of one condition estimate, freed on every return path.
+struct TempAllocs {
+  hipStream_t stream = nullptr;
+  void *p[8] = {};
+  int n = 0;
+  hipError_t get(void **out, size_t bytes) {
+    void *q = nullptr;
+    hipError_t e = hipMalloc(&q, bytes ? bytes : 16);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return e;
+    }
+    p[n++] = q;
+    *out = q;
+    return hipSuccess;
+  }
+  ~TempAllocs() {
+    (void)hipStreamSynchronize(stream);  // nothing queued may still use them
+    for (int i = 0; i < n; ++i) (void)hipFree(p[i]);
+  }
+};
+
+// Lanczos on the smaller Gram matrix of every Fhat_k: when Nd <= Nm,
+// G_k = Fhat_k Fhat_k^H (conjugate-transpose product, then the plain one),
+// else G_k = Fhat_k^H Fhat_k (the other order).
+int condition_impl(fftmv_plan_s *p, int iters, double *kappa, double *smax, double *smin, hipStream_t s) {
+  const int64_t K = p->K, Nm = p->Nm, Nd = p->Nd;
+  const bool wide = Nd <= Nm;
+  const int64_t n = wide ? Nd : Nm, nlong = wide ? Nm : Nd;
+  int64_t J = iters > 0 ? iters : std::min<int64_t>(n, 128);
+  J = std::min<int64_t>(std::min<int64_t>(J, n), kMaxLanczos);
+  const bool f32 = p->fhat64 == nullptr;  // use the complex128 copy when there is one
+  const int64_t ldq = padded_ld(n), ldl = padded_ld(nlong);
+  const size_t csz = f32 ? 8 : 16;
+
+  TempAllocs t;
+  t.stream = s;
+  LanczosArgs a;
+  a.K = K;
+  a.n = n;
+  a.ldq = ldq;
+  a.ldz = ldq;
+  a.ldx = ldq;
+  a.x_f32 = f32;
+  void *Q = nullptr, *z = nullptr, *xin = nullptr, *y = nullptr, *al = nullptr, *be = nullptr, *len = nullptr,
+       *sig = nullptr;
+  const size_t vec = static_cast<size_t>(K * ldq);
+  FFTMV_TRY(t.get(&Q, static_cast<size_t>(J + 1) * vec * 16));
+  FFTMV_TRY(t.get(&z, vec * 16));
+  FFTMV_TRY(t.get(&xin, vec * csz));
+  FFTMV_TRY(t.get(&y, static_cast<size_t>(K * ldl) * csz));
+  FFTMV_TRY(t.get(&al, static_cast<size_t>(J * K) * 8));
+  FFTMV_TRY(t.get(&be, static_cast<size_t>(J * K) * 8));
+  FFTMV_TRY(t.get(&len, static_cast<size_t>(K) * 4));
+  FFTMV_TRY(t.get(&sig, static_cast<size_t>(K) * 16));
+  // the GEMVs read whole 16-byte vectors: padding entries must hold zeros
+  FFTMV_TRY(hipMemsetAsync(xin, 0, vec * csz, s));
+  FFTMV_TRY(hipMemsetAsync(y, 0, static_cast<size_t>(K * ldl) * csz, s));
+  a.Q = static_cast<double *>(Q);
+  a.z = static_cast<double *>(z);
+  a.xin = xin;
+  a.alpha = static_cast<double *>(al);
+  a.beta = static_cast<double *>(be);
+  a.len = static_cast<int *>(len);
+
+  SbgemvArgs g1, g2;
+  g1.K = g2.K = K;
+  g1.Nd = g2.Nd = Nd;
+  g1.Nm = g2.Nm = Nm;
+  g1.F = g2.F = f32 ? p->fhat32 : p->fhat64;
+  g1.ldF = g2.ldF = f32 ? p->ldF32 : p->ldF64;
+  g1.x = xin;
+  g1.ldx = ldq;
+  g1.x_f32 = f32;
+  g1.y = y;
+  g1.ldy = ldl;
+  g1.y_f32 = f32;
+  g2.x = y;
+  g2.ldx = ldl;
+  g2.x_f32 = f32;
+  g2.y = z;
+  g2.ldy = ldq;
+  g2.y_f32 = false;
+
+  FFTMV_TRY(launch_lanczos_start(a, s));
+  for (int j = 0; j < J; ++j) {
+    if (wide) {
+      FFTMV_TRY(launch_sbgemv_c(g1, f32, s));
+      FFTMV_TRY(launch_sbgemv_n(g2, f32, s));
+    } else {
+      FFTMV_TRY(launch_sbgemv_n(g1, f32, s));
+      FFTMV_TRY(launch_sbgemv_c(g2, f32, s));
+    }
+    FFTMV_TRY(launch_lanczos_step(a, j, s));
+  }
+  FFTMV_TRY(launch_lanczos_extremes(a, static_cast<double *>(sig), s));
+  double *h = new (std::nothrow) double[2 * K];
+  if (!h) return FFTMV_ERR_INTERNAL;
+  hipError_t e = hipMemcpyAsync(h, sig, static_cast<size_t>(K) * 16, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete[] h;
+    return status_from_hip(e);
+  }
+  double hi = 0.0, lo = INFINITY;
+  for (int64_t k = 0; k < K; ++k) {
+    hi = std::max(hi, h[2 * k]);
+    lo = std::min(lo, h[2 * k + 1]);
+    if (smax) smax[k] = h[2 * k];
+    if (smin) smin[k] = h[2 * k + 1];
+  }
+  delete[] h;
+  if (kappa) *kappa = lo > 0.0 ? hi / lo : INFINITY;
+  return FFTMV_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -420,6 +537,7 @@ const char *fftmv_status_string(int status) {
     case FFTMV_ERR_OUT_OF_MEMORY: return "out of device memory";
     case FFTMV_ERR_HIP: return "HIP runtime error";
     case FFTMV_ERR_INTERNAL: return "internal error";
+    case FFTMV_ERR_NO_CONFIG: return "no precision configuration meets the error tolerance";
     default: return "unknown status";
   }
 }
@@ -481,6 +599,16 @@ int fftmv_buffer(fftmv_plan_t plan, int which, void **ptr, int64_t *ld, int *ele
   if (ld) *ld = l;
   if (elem_bytes) *elem_bytes = eb;
   return FFTMV_SUCCESS;
+}
+
+int fftmv_condition(fftmv_plan_t plan, int iters, double *kappa, double *sigma_max, double *sigma_min,
+                    hipStream_t stream) {
+  if (!plan) return FFTMV_ERR_INVALID_ARG;
+  try {
+    return condition_impl(plan, iters, kappa, sigma_max, sigma_min, stream);
+  } catch (...) {
+    return FFTMV_ERR_INTERNAL;
+  }
 }
 
 int fftmv_version(void) { return kVersion; }

@@ -70,6 +70,8 @@ extern "C" {
 #define FFTMV_ERR_OUT_OF_MEMORY (-3)    /* device allocation failed           */
 #define FFTMV_ERR_HIP (-4)              /* a HIP runtime call or launch failed */
 #define FFTMV_ERR_INTERNAL (-5)         /* unexpected library condition       */
+#define FFTMV_ERR_NO_CONFIG (-6)        /* no precision configuration meets the
+                                           error tolerance                    */
 
 /* ------------------------------------------------------- precision mask
  * Bit (5*dir + stage - 1) set = that stage runs in FP32, clear = FP64.
@@ -154,6 +156,98 @@ FFTMV_API int fftmv_run_stages(fftmv_plan_t plan, int dir, int first, int last, 
  * buffers between two stages are stored in the narrower of the two stages'
  * precisions. Any out pointer may be NULL. */
 FFTMV_API int fftmv_buffer(fftmv_plan_t plan, int which, void **ptr, int64_t *ld, int *elem_bytes);
+
+/* ---------------------------------------------- precision selection
+ * "Mixed-precision FFTMatvec performance optimization on AMD GPUs",
+ * section 1.1, bounds the relative error of an apply by
+ *
+ *   kappa(Fhat) [ c1 e1 + (cF ed + c2 e2 + c4 e4) log2(Nt) + c3 e3 n
+ *                 + c5 e5 log2(pc) ]
+ *
+ * where e_s is the unit roundoff of stage s (2^-24 in FP32, 2^-53 in FP64),
+ * ed = 2^-53 that of the FP64 setup transform, n the length of the
+ * SBGEMV's inner products and pc the number of processor columns of the
+ * distributed form. Section 2.1 selects a configuration from an error
+ * predictor (this bound), a performance predictor and a search of the
+ * Pareto front of the candidates that meet the tolerance; section 2.2 runs
+ * it over the 32 configurations (5 stages x 2 precisions) of a direction.
+ *
+ * The page prints no constants. Here they are parameters (defaults fitted
+ * to measured errors), and these readings complete the bound:
+ *   - n = Nm for F and Nd for F* (the inner length of each direction's
+ *     SBGEMV); each direction has its own constants;
+ *   - on one GPU pc = 1, where log2(pc) = 0 would make an FP32 stage 5
+ *     free of error although it rounds the output once; the stage-5 term is
+ *     taken as c5 e5 max(1, log2(pc)).
+ * The performance predictor is a bandwidth model: each kernel of the apply
+ * moves its algorithmic bytes through HBM at a sustained bandwidth B, each
+ * batched FFT moves its tile through LDS once per radix pass (write and
+ * read, Nt complex values per channel in the FFT stage's precision) at
+ * B_lds, and each kernel adds a fixed time t0. Stage-boundary buffers hold
+ * the narrower precision of their two stages, and the fused form (default)
+ * folds stage 1 into the forward FFT's loads and stage 5 into the inverse
+ * FFT's stores.
+ *
+ * Model parameters, FFTMV_MODEL_PARAMS doubles:
+ *   [0..4] c1..c5   [5] cF   [6] B, [7] B_lds in bytes/s   [8] t0 in s
+ * A configuration ("stage bits") is 5 bits for one direction, bit s-1 set
+ * when stage s is FP32; its place in a plan mask is bits << (5*dir).
+ * These functions are host-only and touch no device. */
+#define FFTMV_MODEL_PARAMS 9
+
+/* The library's default model parameters for direction dir (constants
+ * fitted on one MI355X at Nm=5000, Nd=100, Nt=1000). */
+FFTMV_API int fftmv_model_defaults(int dir, double *params);
+
+/* Predicted relative error and apply time (seconds) of one configuration.
+ *   flags   FFTMV_FLAG_STAGED selects the five-kernel byte model
+ *   kappa   condition number of Fhat (fftmv_condition), >= 1
+ *   params  FFTMV_MODEL_PARAMS values, or NULL for the defaults
+ * Either output may be NULL. FFTMV_ERR_INVALID_ARG for sizes < 1, dir not
+ * 0/1, stage_bits > 31, kappa < 1 or NaN, or parameters out of range
+ * (negative constants, bandwidths <= 0); FFTMV_ERR_UNSUPPORTED_SIZE for an
+ * Nt that fftmv_setup rejects. The same checks apply to the two calls
+ * below. */
+FFTMV_API int fftmv_predict(int64_t Nm, int64_t Nd, int64_t Nt, int dir, uint32_t stage_bits, uint32_t flags,
+                            double kappa, const double *params, double *est_error, double *est_seconds);
+
+/* Pareto front of the configurations of direction dir whose predicted
+ * error is <= error_tol: no other feasible configuration is both faster and
+ * more accurate. front[0..*count-1] (room for 32) is sorted by predicted
+ * time, ties by error, then by fewer FP32 stages. *count = 0 when nothing is
+ * feasible (the call still succeeds). */
+FFTMV_API int fftmv_pareto_front(int64_t Nm, int64_t Nd, int64_t Nt, int dir, uint32_t flags, double kappa,
+                                 double error_tol, const double *params, uint32_t *front, int *count);
+
+/* select_precision(error_tol) of section 2.1: the fastest configuration on
+ * the Pareto front. When no configuration meets the tolerance it returns
+ * FFTMV_ERR_NO_CONFIG and reports the all-FP64 configuration (0) and its
+ * prediction instead. Any output may be NULL. */
+FFTMV_API int fftmv_select_precision(int64_t Nm, int64_t Nd, int64_t Nt, int dir, uint32_t flags, double kappa,
+                                     double error_tol, const double *params, uint32_t *stage_bits,
+                                     double *est_error, double *est_seconds);
+
+/* kappa(Fhat), the condition number in the bound above: Fhat is block
+ * diagonal, so kappa = max_k s_max(Fhat_k) / min_k s_min(Fhat_k) over the
+ * min(Nd, Nm) singular values of each block (+Inf if some block is
+ * singular). Estimated on the device by `iters` Lanczos steps (with full
+ * reorthogonalisation) on each block's smaller Gram matrix, using the
+ * plan's complex128 Fhat if it holds one, else its complex64 copy;
+ * iters <= 0 picks min(n, 128), and iters is capped at min(n, 512) with
+ * n = min(Nd, Nm). With iters >= n the values are those of the Gram
+ * matrices up to rounding; with fewer, s_max is a lower and s_min an upper
+ * bound (Ritz values), so kappa is under-estimated. Through the Gram matrix
+ * s_min is resolved down to about sqrt(u) s_max (u the unit roundoff of
+ * the Fhat copy used), so kappa is meaningful up to ~1e7 (complex128) or
+ * ~1e3 (complex64 only).
+ *   kappa      out, may be NULL
+ *   sigma_max, sigma_min   out, host arrays of Nt+1 doubles (per
+ *              frequency), may be NULL
+ * Allocates and frees its own device workspace (~(iters+3) * (Nt+1) *
+ * n * 16 bytes plus one long vector per frequency); synchronises `stream`
+ * before returning. Must be ordered with the plan's applies. */
+FFTMV_API int fftmv_condition(fftmv_plan_t plan, int iters, double *kappa, double *sigma_max, double *sigma_min,
+                              hipStream_t stream);
 
 /* Library version, (major << 16) | (minor << 8) | patch. */
 FFTMV_API int fftmv_version(void);

@@ -15,8 +15,9 @@ sections 1 (block triangular Toeplitz operator), 1.1 (five stages) and 1.2
 Parity pins (tests/test_oracle_*.py): the FFT against a textbook O(N^2) DFT,
 numpy.fft and closed forms; the five stages against the dense product and
 the direct double sum; the adjoint identity; zero, delta, delay, block
-diagonal, Nt = 1 and scalar-convolution special cases. No function here is
-"parity unpinned".
+diagonal, Nt = 1 and scalar-convolution special cases; the condition number
+of Fhat against operators built with known singular values (closed forms).
+No function here is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -173,3 +174,20 @@ def rel_l2(x, ref) -> float:
     den = np.linalg.norm(ref)
     num = np.linalg.norm(x - ref)
     return float(num / den) if den > 0 else float(num)
+
+
+def condition(Fhat):
+    """(kappa, s_max per frequency, s_min per frequency) of Fhat [K][Nd][Nm].
+
+    Section 1.1 scales the error bound by the condition number of Fhat.
+    Fhat is block diagonal with one Nd x Nm block per frequency, so its
+    singular values are those of all the blocks together:
+    kappa = max_k s_max(Fhat_k) / min_k s_min(Fhat_k), each block having
+    min(Nd, Nm) singular values; +inf when a block is singular. numpy's SVD
+    is the step."""
+    Fh = np.asarray(Fhat, dtype=np.complex128)
+    s = np.linalg.svd(Fh, compute_uv=False)
+    smax, smin = s[:, 0], s[:, -1]
+    lo = float(smin.min())
+    kappa = float(smax.max()) / lo if lo > 0 else float("inf")
+    return kappa, smax, smin

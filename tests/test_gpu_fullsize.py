@@ -102,6 +102,13 @@ def test_main_page_masks_separately(fm, main_case):
     check(fm, main_case, fm.FFTMV_MIXED_FADJ, 1e-6, flags=fm.FFTMV_FLAG_FHAT_BOTH)
 
 
+def test_main_fp32_pad_ahead_of_fp64_fft(fm, main_case):
+    """Stage 1 in FP32 (input rounded to binary32) ahead of an FP64 FFT, the
+    rest FP64: the wide-batch transform with input rounding."""
+    mask = fm.FFTMV_FP32(0, 1) | fm.FFTMV_FP32(1, 1)
+    check(fm, main_case, mask, 1e-6)
+
+
 @pytest.mark.slow
 def test_scale_share_mixed(fm):
     """One GPU's share of a large grid: Nm=20000, Nd=100, Nt=2000, F̂ ~32 GB
