@@ -60,6 +60,7 @@ def parse():
     ap.add_argument("--mask", type=lambda s: int(s, 0), default=0x186)
     ap.add_argument("--staged", action="store_true", help="five-kernel form (pad/unpad materialised)")
     ap.add_argument("--kernel-reps", type=int, default=20, help="stage-3-only launches timed for the roofline")
+    ap.add_argument("--setup-reps", type=int, default=3, help="extra plan setups timed after the first")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-cols", type=int, default=0, help="oracle sample: input columns (0 = Nm/5)")
     ap.add_argument("--no-check", action="store_true", help="skip the spot-step check against the oracle")
@@ -193,6 +194,15 @@ def main():
     t0 = time.perf_counter()
     plan = fm.Plan(F_dev, mask | flags)
     setup_s = time.perf_counter() - t0
+    # setup again on a warm allocator: the time of fftmv_setup itself
+    # (allocation, zero fills, the FP64 transform of F, synchronisation)
+    setup_ms = []
+    for _ in range(args.setup_reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        extra = fm.Plan(F_dev, mask | flags)
+        setup_ms.append((time.perf_counter() - t0) * 1e3)
+        extra.close()
     del F_dev
     torch.cuda.empty_cache()
     v_dev = torch.empty((Nt, Nd), dtype=torch.float64, device=dev)
@@ -301,6 +311,7 @@ def main():
         "check": check,
         "context": {"page_mi355x_f_apply_ms": {"fp64": 1.9, "mixed": 1.3}},
         "setup_s": round(setup_s, 3),
+        "setup_ms": {"first": round(setup_s * 1e3, 2), "repeats": [round(x, 2) for x in setup_ms]},
     }
     print(json.dumps(out), flush=True)
     plan.close()

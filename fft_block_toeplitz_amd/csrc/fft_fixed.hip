@@ -155,11 +155,14 @@ __device__ __forceinline__ void ct_last_pass(const cx<T> *lds, const cx<T> *__re
   }
 }
 
-// Forward transform of FP64 input, length L = Nt, into complex64 or
-// complex128 (apply path: one output row per frequency, 32-bit offsets).
+// Forward transform of FP64 input, length L = Nt, into complex64 and/or
+// complex128.
 // ROUND: an FP64 transform of samples first rounded to binary32 (an FP32
 // stage 1 ahead of an FP64 stage 2); FP32 transforms round on conversion.
-template <typename T, int L, int C, int TPB, bool NTS, bool ROUND>
+// SETUP = false: the apply path -- one output row per frequency, 32-bit
+// offsets. SETUP = true: the frequency blocks -- channel ch goes to row
+// ch / cpr, column ch % cpr of its frequency's block, 64-bit offsets.
+template <typename T, int L, int C, int TPB, bool NTS, bool ROUND, bool SETUP = false>
 __global__ __launch_bounds__(TPB) void rfft_forward_ct(FwdFftArgs a, const cx<T> *__restrict__ tw,
                                                        int64_t nblocks) {
   constexpr FftGeom g = make_geometry(L);
@@ -175,8 +178,8 @@ __global__ __launch_bounds__(TPB) void rfft_forward_ct(FwdFftArgs a, const cx<T>
     const int t0 = 2 * n;  // t0 < L = Nt is guaranteed for n < NZ, L even or odd
     T re = T(0), im = T(0);
     if (live) {
-      double x0 = load_elem<true>(src, t0 * ld + ch), x1 = 0.0;
-      if (t0 + 1 < L) x1 = load_elem<true>(src, (t0 + 1) * ld + ch);
+      double x0 = load_elem<!SETUP>(src, t0 * ld + ch), x1 = 0.0;
+      if (t0 + 1 < L) x1 = load_elem<!SETUP>(src, (t0 + 1) * ld + ch);
       if constexpr (ROUND) {
         x0 = round_f32(x0);
         x1 = round_f32(x1);
@@ -198,9 +201,29 @@ __global__ __launch_bounds__(TPB) void rfft_forward_ct(FwdFftArgs a, const cx<T>
   const int c0 = (threadIdx.x % CP) * NC;
   const int64_t ch0 = tile * C + c0;
   if (ch0 >= a.nchan) return;
-  const bool two = NC == 2 && ch0 + 1 < a.nchan;
+  // output position of channel ch0 (and ch0 + 1 right after it when both
+  // are in one row)
+  int64_t o32 = ch0, o64 = ch0;
+  bool two = NC == 2 && ch0 + 1 < a.nchan;
+  if constexpr (SETUP) {
+    const int64_t row = ch0 / a.cpr, col = ch0 - row * a.cpr;
+    o32 = row * a.ldr32 + col;
+    o64 = row * a.ldr64 + col;
+    // a 16-byte pair store needs both channels in one row and an even
+    // complex64 position (rows of odd length put odd channels at odd ones)
+    two = two && col + 1 < a.cpr && (o32 & 1) == 0;
+  }
   cx<float> *d32 = static_cast<cx<float> *>(a.dst32);
   cx<double> *d64 = static_cast<cx<double> *>(a.dst64);
+  int64_t o32b = o32 + 1, o64b = o64 + 1;  // the second channel's position
+  if constexpr (SETUP) {
+    if (NC == 2 && ch0 + 1 < a.nchan) {  // ch0 + 1 may start the next row
+      const int64_t row = (ch0 + 1) / a.cpr, col = ch0 + 1 - row * a.cpr;
+      o32b = row * a.ldr32 + col;
+      o64b = row * a.ldr64 + col;
+    }
+  }
+  const bool second = NC == 2 && ch0 + 1 < a.nchan;
   for (int b = threadIdx.x; b < (L + 1) * CP; b += TPB) {
     const int k = b / CP;
     const int ka = k == L ? 0 : k, kb = k == 0 ? 0 : L - k;
@@ -214,16 +237,18 @@ __global__ __launch_bounds__(TPB) void rfft_forward_ct(FwdFftArgs a, const cx<T>
       x[e] = ev + cmul(mk(dd.im * T(0.5), -dd.re * T(0.5)), w);
     }
     if (d32) {
-      cx<float> *p = d32 + k * a.fstride32 + ch0;
-      if (two)
-        store_pair<NTS>(p, cvt<float>(x[0]), cvt<float>(x[NC - 1]));
-      else
-        store_one<NTS>(p, cvt<float>(x[0]));
+      cx<float> *p = d32 + k * a.fstride32;
+      if (two) {
+        store_pair<NTS>(p + o32, cvt<float>(x[0]), cvt<float>(x[NC - 1]));
+      } else {
+        store_one<NTS>(p + o32, cvt<float>(x[0]));
+        if (second) store_one<NTS>(p + o32b, cvt<float>(x[NC - 1]));
+      }
     }
     if (d64) {
-      cx<double> *p = d64 + k * a.fstride64 + ch0;
-      store_one<NTS>(p, cvt<double>(x[0]));
-      if (two) store_one<NTS>(p + 1, cvt<double>(x[NC - 1]));
+      cx<double> *p = d64 + k * a.fstride64;
+      store_one<NTS>(p + o64, cvt<double>(x[0]));
+      if (second) store_one<NTS>(p + o64b, cvt<double>(x[NC - 1]));
     }
   }
 }
@@ -312,6 +337,26 @@ void launch_fwd_ct_c(const FwdFftArgs &a, const void *tw, hipStream_t s) {
     launch_fwd_ct<T, L, ROUND, 1>(a, tw, s);
 }
 
+// the frequency blocks (setup): FP64 transform, 64-bit offsets, rows of cpr
+// channels. Plain (cached) stores: nothing follows in the same stream that
+// the written lines could slow down, and partial lines of neighbouring
+// tiles merge in L2 instead of reaching HBM twice. At Nt = 1000 the tile
+// holds 8 channels (144 KB of LDS), so every time step of F is read in
+// 64-byte runs; at Nt = 2000 four channels already fill the LDS.
+template <int L>
+void launch_fwd_ct_setup(const FwdFftArgs &a, const void *tw, hipStream_t s) {
+  constexpr int C = L == 1000 ? 8 : 4, TPB = 1024;
+  const cx<double> *t = static_cast<const cx<double> *>(tw);
+  if (a.nchan >= kWideBatch) {
+    const int64_t nblocks = (a.nchan + C - 1) / C;
+    hipLaunchKernelGGL((rfft_forward_ct<double, L, C, TPB, false, false, true>), dim3(static_cast<unsigned>(nblocks)),
+                       dim3(TPB), 0, s, a, t, nblocks);
+  } else {
+    hipLaunchKernelGGL((rfft_forward_ct<double, L, 1, kBlock, false, false, true>),
+                       dim3(static_cast<unsigned>(a.nchan)), dim3(kBlock), 0, s, a, t, a.nchan);
+  }
+}
+
 template <int L>
 void launch_fwd_ct_any(const FwdFftArgs &a, bool compute_f32, const void *tw, hipStream_t s) {
   if (compute_f32)
@@ -363,7 +408,17 @@ bool inv_ct_applies(const FftGeom &g, const InvFftArgs &a) {
 
 bool launch_fft_forward_fixed(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s) {
-  if (!fwd_ct_applies(g, a)) return false;
+  if (!fwd_ct_applies(g, a)) {
+    // the frequency blocks: FP64 input and transform, any row structure and size
+    const bool setup = has_ct(g.L) && a.Nt == g.L && !a.src_f32 && !a.round_f32 && !compute_f32 &&
+                       a.nchan <= a.src_ld && a.cpr >= 1 && (a.nchan + kWideBatch) / 4 < INT32_MAX;
+    if (!setup) return false;
+    if (g.L == 1000)
+      launch_fwd_ct_setup<1000>(a, tw, s);
+    else
+      launch_fwd_ct_setup<2000>(a, tw, s);
+    return true;
+  }
   if (g.L == 1000)
     launch_fwd_ct_any<1000>(a, compute_f32, tw, s);
   else

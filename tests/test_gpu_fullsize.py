@@ -83,6 +83,27 @@ def check(fm, c, mask, tol, flags=0, repeat=False):
     plan.close()
 
 
+def test_main_fhat_sampled_rows(fm, main_case):
+    """The frequency blocks as the setup builds them at full size (both
+    stored precisions), on three sampled rows r against the oracle's
+    transform of those rows' series."""
+    c = main_case
+    rows = [0, 37, 99]
+    ref = oracle.setup(np.ascontiguousarray(c.F[:, rows, :]))
+    plan = fm.Plan(c.F_dev, fm.FFTMV_MIXED | fm.FFTMV_FLAG_FHAT_BOTH)
+    Nm, Nd, Nt = c.shape.Nm, c.shape.Nd, c.shape.Nt
+    for which, tol in ((1, 1e-13), (0, 1e-7)):
+        full = plan.read_buffer(which).reshape(Nt + 1, Nd, -1)
+        got = full[:, rows, :Nm].cpu().numpy()
+        pad = full[:, rows, Nm:].abs().max().item() if which == 0 and full.shape[2] > Nm else 0.0
+        del full
+        torch.cuda.empty_cache()
+        e = oracle.rel_l2(got, ref)
+        note(f"Fhat {'c128' if which else 'c64'} sampled rows: rel err {e:.3e}")
+        assert e <= tol and pad == 0.0
+    plan.close()
+
+
 def test_main_mixed_as_benchmarked(fm, main_case):
     check(fm, main_case, fm.FFTMV_MIXED, 1e-6, repeat=True)
 

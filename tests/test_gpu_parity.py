@@ -110,7 +110,11 @@ def test_apply_matches_oracle(fm, shape, mask, staged):
     plan.close()
 
 
-@pytest.mark.parametrize("shape", [(8, 4, 16), (500, 20, 256), (37, 5, 20)])
+@pytest.mark.parametrize("shape", [(8, 4, 16), (500, 20, 256), (37, 5, 20),
+                                   (129, 65, 1000),   # wide batch, fixed-length setup kernel
+                                   (37, 111, 1000),   # wide batch, odd rows: channel pairs straddle rows
+                                   (33, 7, 2000),     # narrow batch, Nt = 2000
+                                   (2048, 2, 2000)])  # wide batch, Nt = 2000, 256-byte aligned rows
 def test_fhat_matches_oracle(fm, shape):
     c = case(*shape)
     Nm, Nd, Nt = shape
