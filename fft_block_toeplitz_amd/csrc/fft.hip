@@ -17,7 +17,7 @@
 // consecutive channels: global loads and stores along a time step or a
 // frequency are contiguous over the C channels, and LDS accesses are
 // stride-1 across lanes. The length-L complex FFT is a Stockham autosort
-// (self-sorting, no bit reversal) with radix 2/4/5/8 passes; each pass reads
+// (self-sorting, no bit reversal) with radix 2/3/4/5/7/8 passes; each pass reads
 // all its butterfly inputs into registers, synchronises, then writes in
 // place. The first pass takes its inputs straight from global memory (all
 // of a thread's loads in flight at once) and, in the inverse, the last pass
@@ -138,8 +138,10 @@ __device__ __forceinline__ void middle_passes(cx<T> *lds, const FftGeom &g, int 
   for (int p = first; p < last; ++p) {
     switch (g.radix[p]) {
       case 2: lds_pass<T, 2, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+      case 3: lds_pass<T, 3, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
       case 4: lds_pass<T, 4, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
       case 5: lds_pass<T, 5, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+      case 7: lds_pass<T, 7, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
       default: lds_pass<T, 8, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
     }
   }
@@ -149,8 +151,10 @@ template <typename T, int S, int VMAX, typename Get, typename Put>
 __device__ __forceinline__ void first_pass_any(int R, int L, int logC, Get get, Put put) {
   switch (R) {
     case 2: first_pass<T, 2, S, VMAX>(L, logC, get, put); break;
+    case 3: first_pass<T, 3, S, VMAX>(L, logC, get, put); break;
     case 4: first_pass<T, 4, S, VMAX>(L, logC, get, put); break;
     case 5: first_pass<T, 5, S, VMAX>(L, logC, get, put); break;
+    case 7: first_pass<T, 7, S, VMAX>(L, logC, get, put); break;
     default: first_pass<T, 8, S, VMAX>(L, logC, get, put); break;
   }
 }
@@ -160,8 +164,10 @@ __device__ __forceinline__ void last_pass_any(int R, const cx<T> *lds, int L, in
                                               const cx<T> *__restrict__ tw, Put put) {
   switch (R) {
     case 2: last_pass<T, 2, S, VMAX>(lds, L, logC, twstep, tw, put); break;
+    case 3: last_pass<T, 3, S, VMAX>(lds, L, logC, twstep, tw, put); break;
     case 4: last_pass<T, 4, S, VMAX>(lds, L, logC, twstep, tw, put); break;
     case 5: last_pass<T, 5, S, VMAX>(lds, L, logC, twstep, tw, put); break;
+    case 7: last_pass<T, 7, S, VMAX>(lds, L, logC, twstep, tw, put); break;
     default: last_pass<T, 8, S, VMAX>(lds, L, logC, twstep, tw, put); break;
   }
 }

@@ -19,6 +19,19 @@ __device__ __forceinline__ void dft2(cx<T> &a, cx<T> &b) {
 }
 
 template <int S, typename T>
+__device__ __forceinline__ void dft3(cx<T> *x) {
+  // y_{1,2} = x0 - (x1 + x2)/2 +- S i sin(2 pi / 3) (x1 - x2)
+  const T h = T(0.86602540378443864676372317075293618347);  // sqrt(3)/2
+  cx<T> t = x[1] + x[2];
+  cx<T> m = mk(x[0].re - T(0.5) * t.re, x[0].im - T(0.5) * t.im);
+  cx<T> d = x[1] - x[2];
+  d = mul_si<S>(mk(h * d.re, h * d.im));
+  x[0] = x[0] + t;
+  x[1] = m + d;
+  x[2] = m - d;
+}
+
+template <int S, typename T>
 __device__ __forceinline__ void dft4(cx<T> &x0, cx<T> &x1, cx<T> &x2, cx<T> &x3) {
   cx<T> t0 = x0 + x2, t1 = x0 - x2, t2 = x1 + x3, t3 = mul_si<S>(x1 - x3);
   x0 = t0 + t2;
@@ -71,11 +84,44 @@ __device__ __forceinline__ void dft5(cx<T> *x) {
   x[3] = a2 - b2;
 }
 
+template <int S, typename T>
+__device__ __forceinline__ void dft7(cx<T> *x) {
+  // pairs (p, 7 - p): y_q = a_q + S i b_q and y_{7-q} = a_q - S i b_q with
+  // a_q = x0 + sum_p (x_p + x_{7-p}) cos(2 pi p q / 7),
+  // b_q = sum_p (x_p - x_{7-p}) sin(2 pi p q / 7), p, q = 1..3
+  const T c1 = T(0.62348980185873353052500488400423981063);   // cos(2 pi / 7)
+  const T c2 = T(-0.22252093395631440428890256449679475947);  // cos(4 pi / 7)
+  const T c3 = T(-0.90096886790241912623610231950744505117);  // cos(6 pi / 7)
+  const T s1 = T(0.78183148246802980870844452667405775023);   // sin(2 pi / 7)
+  const T s2 = T(0.97492791218182360701813168299393121723);   // sin(4 pi / 7)
+  const T s3 = T(0.43388373911755812047576833284835875461);   // sin(6 pi / 7)
+  const cx<T> t1 = x[1] + x[6], t2 = x[2] + x[5], t3 = x[3] + x[4];
+  const cx<T> u1 = x[1] - x[6], u2 = x[2] - x[5], u3 = x[3] - x[4];
+  auto lin = [](T a, cx<T> p, T b, cx<T> q, T c, cx<T> r) {
+    return mk(a * p.re + b * q.re + c * r.re, a * p.im + b * q.im + c * r.im);
+  };
+  const cx<T> a1 = x[0] + lin(c1, t1, c2, t2, c3, t3);
+  const cx<T> a2 = x[0] + lin(c2, t1, c3, t2, c1, t3);
+  const cx<T> a3 = x[0] + lin(c3, t1, c1, t2, c2, t3);
+  const cx<T> b1 = mul_si<S>(lin(s1, u1, s2, u2, s3, u3));
+  const cx<T> b2 = mul_si<S>(lin(s2, u1, -s3, u2, -s1, u3));
+  const cx<T> b3 = mul_si<S>(lin(s3, u1, -s1, u2, s2, u3));
+  x[0] = x[0] + t1 + t2 + t3;
+  x[1] = a1 + b1;
+  x[6] = a1 - b1;
+  x[2] = a2 + b2;
+  x[5] = a2 - b2;
+  x[3] = a3 + b3;
+  x[4] = a3 - b3;
+}
+
 template <int R, int S, typename T>
 __device__ __forceinline__ void dft(cx<T> *x) {
   if constexpr (R == 2) dft2<S>(x[0], x[1]);
+  else if constexpr (R == 3) dft3<S>(x);
   else if constexpr (R == 4) dft4<S>(x[0], x[1], x[2], x[3]);
   else if constexpr (R == 5) dft5<S>(x);
+  else if constexpr (R == 7) dft7<S>(x);
   else dft8<S>(x);
 }
 

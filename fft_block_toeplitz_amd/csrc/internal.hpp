@@ -20,16 +20,19 @@ struct FftGeom {
   int twstep[kMaxPasses] = {};  // 2L / (ns * radix): exponent step in the w_{2L} table
 };
 
-// Radix schedule for L = 2^a 5^b: radix 8 while more than four factors of
-// two remain, then 4 4 / 8 / 4 / 2, then the fives. Usable on the host and,
-// as a constant expression, in kernels specialised for one length.
+// Radix schedule for L = 2^a 3^b 5^c 7^d: radix 8 while more than four
+// factors of two remain, then 4 4 / 8 / 4 / 2, then the threes, fives and
+// sevens. Usable on the host and, as a constant expression, in kernels
+// specialised for one length.
 constexpr FftGeom make_geometry(int L) {
   FftGeom g{};
   if (L < 1) return g;
-  int r = L, a = 0, b = 0;
+  int r = L, a = 0, b3 = 0, b = 0, b7 = 0;
   while (r % 2 == 0) r /= 2, ++a;
+  while (r % 3 == 0) r /= 3, ++b3;
   while (r % 5 == 0) r /= 5, ++b;
-  if (r != 1) return g;
+  while (r % 7 == 0) r /= 7, ++b7;
+  if (r != 1 || a / 3 + 2 + b3 + b + b7 > kMaxPasses) return g;
   int np = 0;
   while (a > 4) {
     g.radix[np++] = 8;
@@ -45,7 +48,9 @@ constexpr FftGeom make_geometry(int L) {
   } else if (a == 1) {
     g.radix[np++] = 2;
   }
+  for (int i = 0; i < b3; ++i) g.radix[np++] = 3;
   for (int i = 0; i < b; ++i) g.radix[np++] = 5;
+  for (int i = 0; i < b7; ++i) g.radix[np++] = 7;
   g.L = L;
   g.npass = np;
   int ns = 1;

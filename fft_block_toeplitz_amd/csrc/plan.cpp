@@ -541,7 +541,7 @@ const char *fftmv_status_string(int status) {
   switch (status) {
     case FFTMV_SUCCESS: return "success";
     case FFTMV_ERR_INVALID_ARG: return "invalid argument";
-    case FFTMV_ERR_UNSUPPORTED_SIZE: return "unsupported size (2*Nt must be 2^a*5^b with Nt <= 4096)";
+    case FFTMV_ERR_UNSUPPORTED_SIZE: return "unsupported size (Nt must be 2^a*3^b*5^c*7^d and at most 4096)";
     case FFTMV_ERR_OUT_OF_MEMORY: return "out of device memory";
     case FFTMV_ERR_HIP: return "HIP runtime error";
     case FFTMV_ERR_INTERNAL: return "internal error";

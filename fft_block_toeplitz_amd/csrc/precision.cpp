@@ -72,8 +72,12 @@ double predict_seconds(const Problem &p, uint32_t bits, bool staged, const doubl
   return bytes / c[6] + lds / c[7] + kernels * c[8];
 }
 
-// sizes the library runs: 2 Nt = 2^a 5^b, Nt <= 4096
-bool supported(int64_t Nt) { return Nt >= 1 && Nt <= 4096 && make_geometry(static_cast<int>(Nt)).L == Nt; }
+// the sizes fftmv_setup accepts
+bool supported(int64_t Nt) {
+  if (Nt < 1 || Nt > 4096) return false;
+  const fftmv::FftGeom g = make_geometry(static_cast<int>(Nt));
+  return g.L == Nt && fftmv::fft_channels_per_block(g, false, 1) > 0 && fftmv::fft_channels_per_block(g, true, 1) > 0;
+}
 
 bool valid(int64_t Nm, int64_t Nd, int64_t Nt, int dir, uint32_t flags, double kappa, const double *c) {
   if (Nm < 1 || Nd < 1 || Nt < 1 || (dir != 0 && dir != 1)) return false;

@@ -29,7 +29,10 @@
  * Pointers need 8-byte alignment (natural for double).
  *
  * Supported sizes: 1 <= Nm, Nd <= 2^31 - 1; 1 <= Nt <= 4096 with
- * 2 Nt = 2^a 5^b; any other size returns FFTMV_ERR_UNSUPPORTED_SIZE.
+ * Nt = 2^a 3^b 5^c 7^d (radix 2/4/8, 3, 5 and 7 passes), except the few
+ * lengths whose radix-7 passes need more registers than a workgroup holds
+ * (Nt > 3584 with a factor 7); any other size returns
+ * FFTMV_ERR_UNSUPPORTED_SIZE.
  *
  * Ownership and concurrency:
  *   - fftmv_setup is synchronous: when it returns the frequency blocks are
@@ -66,7 +69,7 @@ extern "C" {
 /* ----------------------------------------------------------------- status */
 #define FFTMV_SUCCESS 0
 #define FFTMV_ERR_INVALID_ARG (-1)      /* null pointer, bad size/mask/stage  */
-#define FFTMV_ERR_UNSUPPORTED_SIZE (-2) /* 2 Nt not 2^a 5^b, or Nt too large  */
+#define FFTMV_ERR_UNSUPPORTED_SIZE (-2) /* Nt not 2^a 3^b 5^c 7^d, or too large */
 #define FFTMV_ERR_OUT_OF_MEMORY (-3)    /* device allocation failed           */
 #define FFTMV_ERR_HIP (-4)              /* a HIP runtime call or launch failed */
 #define FFTMV_ERR_INTERNAL (-5)         /* unexpected library condition       */

@@ -91,6 +91,16 @@ SHAPES = [
     (33, 7, 2000),   # the Scale share's time length, narrow batches
     (3, 2, 4096),    # the longest supported transform, 2Nt = 2^13
     (2, 3, 3125),    # 2Nt = 2 * 5^5
+    # radix-3 and radix-7 passes
+    (5, 3, 3),       # Nt = 3
+    (4, 2, 7),       # Nt = 7
+    (9, 4, 21),      # 3 * 7
+    (6, 5, 63),      # 3^2 * 7
+    (11, 3, 360),    # 2^3 3^2 5
+    (7, 3, 1029),    # 3 * 7^3
+    (3, 2, 2187),    # 3^7
+    (2, 2, 3584),    # 2^9 7: the longest radix-7 length that fits
+    (129, 33, 105),  # 3 5 7, wide batch (many channels per workgroup)
 ]
 
 
@@ -114,7 +124,8 @@ def test_apply_matches_oracle(fm, shape, mask, staged):
                                    (129, 65, 1000),   # wide batch, fixed-length setup kernel
                                    (37, 111, 1000),   # wide batch, odd rows: channel pairs straddle rows
                                    (33, 7, 2000),     # narrow batch, Nt = 2000
-                                   (2048, 2, 2000)])  # wide batch, Nt = 2000, 256-byte aligned rows
+                                   (2048, 2, 2000),   # wide batch, Nt = 2000, 256-byte aligned rows
+                                   (9, 4, 21)])       # radix 3 and 7
 def test_fhat_matches_oracle(fm, shape):
     c = case(*shape)
     Nm, Nd, Nt = shape
@@ -175,7 +186,7 @@ def test_stage_by_stage(fm, mask):
     plan.close()
 
 
-@pytest.mark.parametrize("shape", [(37, 5, 20), (37, 5, 1000)])
+@pytest.mark.parametrize("shape", [(37, 5, 20), (37, 5, 1000), (37, 5, 63)])
 def test_all_precision_masks(fm, shape):
     """Every one of the 32 per-stage precision choices of each direction,
     on one plan holding Fhat in both precisions."""
