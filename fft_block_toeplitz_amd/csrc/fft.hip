@@ -178,13 +178,20 @@ __device__ __forceinline__ T to_compute(Src v) {
 }
 
 // --------------------------------------------------------------- forward
-template <typename T, typename Src, bool ROUND, int VMAX, bool OFF32>
+// BLUE: the length-L complex FFT in Bluestein form over an M-point tile
+// (g is then the schedule of M; tw stays the w_{2L} table, twM is w_{2M},
+// hM the filter's transform).
+template <typename T, typename Src, bool ROUND, int VMAX, bool OFF32, bool BLUE>
 __global__ __launch_bounds__(kBlock) void rfft_forward_kernel(FftGeom g, FwdFftArgs a, int logC,
-                                                              const cx<T> *__restrict__ tw, int64_t nblocks) {
+                                                              const cx<T> *__restrict__ tw, int64_t nblocks,
+                                                              const cx<T> *__restrict__ twM,
+                                                              const cx<T> *__restrict__ hM) {
   extern __shared__ __align__(16) unsigned char smem[];
   cx<T> *lds = reinterpret_cast<cx<T> *>(smem);
   const int C = 1 << logC;
-  const int L = g.L;
+  const int L = static_cast<int>(a.Nt);
+  // chirp c[m] = exp(-pi i m^2 / L) (m < L <= 2048: m^2 fits 32 bits)
+  auto chirp = [&](int m) { return tw[(m * m) % (2 * L)]; };
   const int c = threadIdx.x & (C - 1);  // fixed per thread: kBlock is a multiple of C
   const int64_t ch = xcd_contiguous_block(blockIdx.x, nblocks) * C + c;
   const bool live = ch < a.nchan;
@@ -201,13 +208,31 @@ __global__ __launch_bounds__(kBlock) void rfft_forward_kernel(FftGeom g, FwdFftA
     return mk(re, im);
   };
   auto to_lds = [&](int n, cx<T> v) { lds[(n << logC) + c] = v; };
-  if (g.npass == 0) {  // L == 1
-    if (threadIdx.x < C) to_lds(0, get(0));
+  if constexpr (BLUE) {
+    // a[n] = z[n] c[n], zero up to M; a * conj(c) by M-point transforms
+    const int M = g.L;
+    auto get_a = [&](int n) { return n < L ? cmul(get(n), chirp(n)) : mk(T(0), T(0)); };
+    first_pass_any<T, -1, VMAX>(g.radix[0], M, logC, get_a, to_lds);
+    __syncthreads();
+    middle_passes<T, -1, VMAX>(lds, g, 1, g.npass, logC, twM);
+    for (int i = threadIdx.x; i < (M << logC); i += kBlock) lds[i] = cmul(lds[i], hM[i >> logC]);
+    __syncthreads();
+    middle_passes<T, +1, VMAX>(lds, g, 0, g.npass, logC, twM);
   } else {
-    first_pass_any<T, -1, VMAX>(g.radix[0], L, logC, get, to_lds);
+    if (g.npass == 0) {  // L == 1
+      if (threadIdx.x < C) to_lds(0, get(0));
+    } else {
+      first_pass_any<T, -1, VMAX>(g.radix[0], L, logC, get, to_lds);
+    }
+    __syncthreads();
+    middle_passes<T, -1, VMAX>(lds, g, 1, g.npass, logC, tw);
   }
-  __syncthreads();
-  middle_passes<T, -1, VMAX>(lds, g, 1, g.npass, logC, tw);
+  // Z[k]: the tile entry (times c[k] in Bluestein form)
+  auto zat = [&](int k, int ch) {
+    cx<T> v = lds[(k << logC) + ch];
+    if constexpr (BLUE) v = cmul(v, chirp(k));
+    return v;
+  };
 
   // X[k] for k = 0..L; each thread takes two adjacent channels of one bin so
   // that the complex64 output goes out as 16-byte stores
@@ -237,7 +262,7 @@ __global__ __launch_bounds__(kBlock) void rfft_forward_kernel(FftGeom g, FwdFftA
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       if (e == 1 && !two) break;
-      cx<T> za = lds[(ka << logC) + c0 + e], zb = conj(lds[(kb << logC) + c0 + e]);
+      cx<T> za = zat(ka, c0 + e), zb = conj(zat(kb, c0 + e));
       cx<T> ev = scale(za + zb, T(0.5));
       cx<T> dd = za - zb;
       cx<T> o = mk(dd.im * T(0.5), -dd.re * T(0.5));  // (za - zb) / 2i
@@ -261,14 +286,16 @@ __global__ __launch_bounds__(kBlock) void rfft_forward_kernel(FftGeom g, FwdFftA
 }
 
 // --------------------------------------------------------------- inverse
-template <typename T, typename Src, int VMAX, bool OFF32>
+template <typename T, typename Src, int VMAX, bool OFF32, bool BLUE>
 __global__ __launch_bounds__(kBlock) void rfft_inverse_kernel(FftGeom g, InvFftArgs a, int logC,
                                                               const cx<T> *__restrict__ tw, T inv_l,
-                                                              int64_t nblocks) {
+                                                              int64_t nblocks, const cx<T> *__restrict__ twM,
+                                                              const cx<T> *__restrict__ hM) {
   extern __shared__ __align__(16) unsigned char smem[];
   cx<T> *lds = reinterpret_cast<cx<T> *>(smem);
   const int C = 1 << logC;
-  const int L = g.L;
+  const int L = static_cast<int>(a.Nt);
+  auto chirp = [&](int m) { return tw[(m * m) % (2 * L)]; };
   const int c = threadIdx.x & (C - 1);
   const int64_t ch = xcd_contiguous_block(blockIdx.x, nblocks) * C + c;
   const bool live = ch < a.nchan;
@@ -314,6 +341,24 @@ __global__ __launch_bounds__(kBlock) void rfft_inverse_kernel(FftGeom g, InvFftA
   };
   auto to_lds = [&](int n, cx<T> v) { lds[(n << logC) + c] = v; };
 
+  if constexpr (BLUE) {
+    // a[k] = Z[k] conj(c[k]), zero up to M; a * c by M-point transforms;
+    // z[n] = conj(c[n]) (a * c)[n]
+    const int M = g.L;
+    auto get_a = [&](int k) { return k < L ? cmulc(get(k), chirp(k)) : mk(T(0), T(0)); };
+    auto put_z = [&](int n, cx<T> v) {
+      if (n < L) put(n, cmulc(v, chirp(n)));
+    };
+    first_pass_any<T, -1, VMAX>(g.radix[0], M, logC, get_a, to_lds);
+    __syncthreads();
+    middle_passes<T, -1, VMAX>(lds, g, 1, g.npass, logC, twM);
+    for (int i = threadIdx.x; i < (M << logC); i += kBlock) lds[i] = cmul(lds[i], hM[i >> logC]);
+    __syncthreads();
+    middle_passes<T, +1, VMAX>(lds, g, 0, g.npass - 1, logC, twM);
+    const int pl = g.npass - 1;
+    last_pass_any<T, +1, VMAX>(g.radix[pl], lds, M, logC, g.twstep[pl], twM, put_z);
+    return;
+  }
   if (g.npass == 0) {  // L == 1
     if (threadIdx.x < C) put(0, get(0));
     return;
@@ -363,60 +408,92 @@ int ilog2(int c) {
   return l;
 }
 
+// g: the tile's schedule (length L, or M in Bluestein form); twM, hM: the
+// Bluestein tables (null otherwise)
 template <typename T, typename Src, bool ROUND>
-void fwd(const FftGeom &g, const FwdFftArgs &a, const FftLaunch &cfg, const void *tw, hipStream_t s) {
+void fwd(const FftGeom &g, const FwdFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
+         const void *hM, hipStream_t s) {
   const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
   const size_t lds = static_cast<size_t>(g.L) * cfg.C * sizeof(cx<T>);
-  hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmax, false>), dim3(static_cast<unsigned>(nblocks)),
-                     dim3(kBlock), lds, s, g, a, ilog2(cfg.C), static_cast<const cx<T> *>(tw), nblocks);
+  const cx<T> *t = static_cast<const cx<T> *>(tw), *tm = static_cast<const cx<T> *>(twM),
+              *h = static_cast<const cx<T> *>(hM);
+  if (hM)
+    hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmax, false, true>), dim3(static_cast<unsigned>(nblocks)),
+                       dim3(kBlock), lds, s, g, a, ilog2(cfg.C), t, nblocks, tm, h);
+  else
+    hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmax, false, false>),
+                       dim3(static_cast<unsigned>(nblocks)), dim3(kBlock), lds, s, g, a, ilog2(cfg.C), t, nblocks,
+                       tm, h);
 }
 
 template <typename T, typename Src>
-void inv(const FftGeom &g, const InvFftArgs &a, const FftLaunch &cfg, const void *tw, hipStream_t s) {
+void inv(const FftGeom &g, const InvFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
+         const void *hM, hipStream_t s) {
   const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
   const size_t lds = static_cast<size_t>(g.L) * cfg.C * sizeof(cx<T>);
-  hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmax, false>), dim3(static_cast<unsigned>(nblocks)), dim3(kBlock),
-                     lds, s, g, a, ilog2(cfg.C), static_cast<const cx<T> *>(tw), T(1) / static_cast<T>(g.L),
-                     nblocks);
+  const cx<T> *t = static_cast<const cx<T> *>(tw), *tm = static_cast<const cx<T> *>(twM),
+              *h = static_cast<const cx<T> *>(hM);
+  const T inv_l = T(1) / static_cast<T>(a.Nt);
+  if (hM)
+    hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmax, false, true>), dim3(static_cast<unsigned>(nblocks)),
+                       dim3(kBlock), lds, s, g, a, ilog2(cfg.C), t, inv_l, nblocks, tm, h);
+  else
+    hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmax, false, false>), dim3(static_cast<unsigned>(nblocks)),
+                       dim3(kBlock), lds, s, g, a, ilog2(cfg.C), t, inv_l, nblocks, tm, h);
 }
 
 }  // namespace
 hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
-                              hipStream_t s) {
-  if (launch_fft_forward_fixed(g, a, compute_f32, tw, s)) return hipGetLastError();
-  const FftLaunch cfg = fft_launch_config(g, compute_f32, a.nchan);
-  if (cfg.C == 0 || (a.nchan + cfg.C - 1) / cfg.C > INT32_MAX) return hipErrorInvalidValue;
+                              hipStream_t s, const BlueTables *blue) {
+  if (!blue && launch_fft_forward_fixed(g, a, compute_f32, tw, s)) return hipGetLastError();
+  const FftGeom &tile = blue ? blue->gM : g;
+  const void *twM = blue ? (compute_f32 ? blue->tw32 : blue->tw64) : nullptr;
+  const void *hM = blue ? (compute_f32 ? blue->hf32 : blue->hf64) : nullptr;
+  const FftLaunch cfg = fft_launch_config(tile, compute_f32, a.nchan);
+  if (cfg.C == 0 || (a.nchan + cfg.C - 1) / cfg.C > INT32_MAX || (blue && !hM)) return hipErrorInvalidValue;
   if (compute_f32) {
     if (a.src_f32)
-      fwd<float, float, false>(g, a, cfg, tw, s);
+      fwd<float, float, false>(tile, a, cfg, tw, twM, hM, s);
     else
-      fwd<float, double, false>(g, a, cfg, tw, s);
+      fwd<float, double, false>(tile, a, cfg, tw, twM, hM, s);
   } else {
     if (a.src_f32)
-      fwd<double, float, false>(g, a, cfg, tw, s);
+      fwd<double, float, false>(tile, a, cfg, tw, twM, hM, s);
     else if (a.round_f32)
-      fwd<double, double, true>(g, a, cfg, tw, s);
+      fwd<double, double, true>(tile, a, cfg, tw, twM, hM, s);
     else
-      fwd<double, double, false>(g, a, cfg, tw, s);
+      fwd<double, double, false>(tile, a, cfg, tw, twM, hM, s);
   }
   return hipGetLastError();
 }
 hipError_t launch_fft_inverse(const FftGeom &g, const InvFftArgs &a, bool compute_f32, const void *tw,
-                              hipStream_t s) {
-  if (launch_fft_inverse_fixed(g, a, compute_f32, tw, s)) return hipGetLastError();
-  const FftLaunch cfg = fft_launch_config(g, compute_f32, a.nchan);
-  if (cfg.C == 0 || (a.nchan + cfg.C - 1) / cfg.C > INT32_MAX) return hipErrorInvalidValue;
+                              hipStream_t s, const BlueTables *blue) {
+  if (!blue && launch_fft_inverse_fixed(g, a, compute_f32, tw, s)) return hipGetLastError();
+  const FftGeom &tile = blue ? blue->gM : g;
+  const void *twM = blue ? (compute_f32 ? blue->tw32 : blue->tw64) : nullptr;
+  const void *hM = blue ? (compute_f32 ? blue->hi32 : blue->hi64) : nullptr;
+  const FftLaunch cfg = fft_launch_config(tile, compute_f32, a.nchan);
+  if (cfg.C == 0 || (a.nchan + cfg.C - 1) / cfg.C > INT32_MAX || (blue && !hM)) return hipErrorInvalidValue;
   if (compute_f32) {
     if (a.src_f32)
-      inv<float, float>(g, a, cfg, tw, s);
+      inv<float, float>(tile, a, cfg, tw, twM, hM, s);
     else
-      inv<float, double>(g, a, cfg, tw, s);
+      inv<float, double>(tile, a, cfg, tw, twM, hM, s);
   } else {
     if (a.src_f32)
-      inv<double, float>(g, a, cfg, tw, s);
+      inv<double, float>(tile, a, cfg, tw, twM, hM, s);
     else
-      inv<double, double>(g, a, cfg, tw, s);
+      inv<double, double>(tile, a, cfg, tw, twM, hM, s);
   }
   return hipGetLastError();
+}
+
+int64_t bluestein_length(int64_t L) {
+  if (L < 2 || L > (int64_t(1) << 20) || make_geometry(static_cast<int>(L)).L == L) return 0;
+  int64_t M = 1;
+  while (M < 2 * L - 1) M *= 2;
+  const FftGeom gM = make_geometry(static_cast<int>(M));
+  if (fft_channels_per_block(gM, false, 1) == 0 || fft_channels_per_block(gM, true, 1) == 0) return 0;
+  return M;
 }
 }  // namespace fftmv

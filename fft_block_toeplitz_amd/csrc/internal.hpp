@@ -62,6 +62,24 @@ constexpr FftGeom make_geometry(int L) {
   return g;
 }
 
+// Bluestein (chirp-z) form of the length-L complex FFT for lengths without
+// a radix schedule: with c[m] = exp(-pi i m^2 / L) = w_{2L}^(m^2 mod 2L),
+//   Z[k] = c[k] sum_n (z[n] c[n]) conj(c[k - n])     (forward)
+//   z[n] = conj(c[n]) sum_k (Z[k] conj(c[k])) c[n - k]   (inverse)
+// each sum a circular convolution of length M (a power of two >= 2L - 1)
+// done as M-point FFT, product with the filter's transform, inverse
+// M-point FFT. Tables in both precisions (pointers to float or double
+// complex).
+struct BlueTables {
+  FftGeom gM;                                   // radix schedule of M
+  const void *tw32 = nullptr, *tw64 = nullptr;  // w_{2M}^t, t < 2M
+  const void *hf32 = nullptr, *hf64 = nullptr;  // transform of conj(c), wrapped, / M (forward)
+  const void *hi32 = nullptr, *hi64 = nullptr;  // transform of c, wrapped, / M (inverse)
+};
+// Smallest power of two >= 2L - 1 when L has no radix schedule (0 if L has
+// one, or if the M-point tile would not fit a workgroup).
+int64_t bluestein_length(int64_t L);
+
 // Batched forward real FFT: nchan channels of Nt real samples (implicitly
 // zero-padded to 2 Nt), channel ch at src[t * src_ld + ch]; writes the Nt+1
 // bins of channel ch at dst + k * fstride + (ch / cpr) * ldr + ch % cpr, in
@@ -125,10 +143,11 @@ FftLaunch fft_launch_config(const FftGeom &g, bool f32, int64_t nchan);
 // if the transform does not fit.
 int fft_channels_per_block(const FftGeom &g, bool f32, int64_t nchan);
 
+// blue: Bluestein tables when the length has no radix schedule, else null
 hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
-                              hipStream_t s);
+                              hipStream_t s, const BlueTables *blue = nullptr);
 hipError_t launch_fft_inverse(const FftGeom &g, const InvFftArgs &a, bool compute_f32, const void *tw,
-                              hipStream_t s);
+                              hipStream_t s, const BlueTables *blue = nullptr);
 // Fixed-length kernels (fft_fixed.hip): launch and return true when one
 // covers this transform, else return false and launch nothing.
 bool launch_fft_forward_fixed(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <complex>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -32,6 +33,8 @@ struct fftmv_plan_s {
   int64_t Nm = 0, Nd = 0, Nt = 0, K = 0;
   uint32_t prec = 0, flags = 0;
   FftGeom geom;
+  bool blue = false;  // Bluestein form (Nt without a radix schedule)
+  BlueTables bt;
   void *fhat32 = nullptr, *fhat64 = nullptr;
   int64_t ldF32 = 0, ldF64 = 0;
   void *tw32 = nullptr, *tw64 = nullptr;
@@ -106,6 +109,29 @@ void unit_root(int64_t t, int64_t N, double *re, double *im) {
   *im = -(ss * s);
 }
 
+// In-place length-n FFT (n a power of two, exponent sign -1) in long
+// double, for the Bluestein filter tables.
+void host_fft(std::complex<long double> *x, int64_t n) {
+  for (int64_t i = 1, j = 0; i < n; ++i) {  // bit-reversal permutation
+    int64_t bit = n >> 1;
+    for (; j & bit; bit >>= 1) j ^= bit;
+    j ^= bit;
+    if (i < j) std::swap(x[i], x[j]);
+  }
+  const long double pi = 3.141592653589793238462643383279502884L;
+  for (int64_t len = 2; len <= n; len <<= 1) {
+    for (int64_t k = 0; k < len / 2; ++k) {
+      const long double ang = -2.0L * pi * static_cast<long double>(k) / static_cast<long double>(len);
+      const std::complex<long double> w(std::cos(ang), std::sin(ang));
+      for (int64_t i = 0; i < n; i += len) {
+        const std::complex<long double> u = x[i + k], v = x[i + k + len / 2] * w;
+        x[i + k] = u + v;
+        x[i + k + len / 2] = u - v;
+      }
+    }
+  }
+}
+
 void release(fftmv_plan_s *p) {
   for (int i = 0; i < p->nalloc; ++i) (void)hipFree(p->allocs[i]);
   p->nalloc = 0;
@@ -125,6 +151,13 @@ hipError_t dev_alloc(fftmv_plan_s *p, void **ptr, size_t bytes) {
 }
 
 bool aligned8(const void *q) { return (reinterpret_cast<uintptr_t>(q) & 7u) == 0; }
+
+struct cx64 {
+  double re, im;
+};
+struct cx32 {
+  float re, im;
+};
 
 // stage-boundary buffer precisions: the narrower of the two stages
 bool buf_f32(uint32_t prec, int dir, int s) { return fp32(prec, dir, s) || fp32(prec, dir, s + 1); }
@@ -182,7 +215,7 @@ hipError_t stage_fft(const fftmv_plan_s *p, int dir, const double *user_in, bool
     a.ldr64 = 0;
   }
   a.cpr = a.nchan;
-  return launch_fft_forward(p->geom, a, cf32, twiddles(p, cf32), s);
+  return launch_fft_forward(p->geom, a, cf32, twiddles(p, cf32), s, p->blue ? &p->bt : nullptr);
 }
 
 // Stage 3: per-frequency GEMV (F) or conjugate-transpose GEMV (F*).
@@ -225,7 +258,7 @@ hipError_t stage_ifft(const fftmv_plan_s *p, int dir, double *user_out, bool to_
     a.dst_f32 = buf_f32(p->prec, dir, 4);
     a.round_f32 = false;
   }
-  return launch_fft_inverse(p->geom, a, cf32, twiddles(p, cf32), s);
+  return launch_fft_inverse(p->geom, a, cf32, twiddles(p, cf32), s, p->blue ? &p->bt : nullptr);
 }
 
 // Stage 5 alone: buf 4 -> FP64 output.
@@ -322,6 +355,58 @@ int setup_impl(fftmv_plan_s *p, const double *F, hipStream_t s) {
     p->ws_bytes += static_cast<size_t>(N) * 24;
   }
 
+  // Bluestein tables: w_{2M}^t, and the transforms (divided by M) of the
+  // wrapped filters conj(c) (forward) and c (inverse), c[m] = w_{2L}^(m^2 mod 2L)
+  if (p->blue) {
+    const int64_t M = p->bt.gM.L, n64 = 4 * M;  // 2M twiddles + M + M filter values
+    std::complex<long double> *h = new (std::nothrow) std::complex<long double>[M];
+    double *t64 = new (std::nothrow) double[2 * n64];
+    float *t32 = new (std::nothrow) float[2 * n64];
+    if (!h || !t64 || !t32) {
+      delete[] h;
+      delete[] t64;
+      delete[] t32;
+      return FFTMV_ERR_INTERNAL;
+    }
+    for (int64_t t = 0; t < 2 * M; ++t) unit_root(t, 2 * M, &t64[2 * t], &t64[2 * t + 1]);
+    for (int64_t m = 0; m < M; ++m) h[m] = 0.0L;
+    for (int64_t m = 0; m < Nt; ++m) {
+      double re, im;
+      unit_root((m * m) % (2 * Nt), 2 * Nt, &re, &im);
+      h[m] = std::complex<long double>(re, -im);  // conj(c[m])
+      if (m > 0) h[M - m] = h[m];                  // c is even in m
+    }
+    host_fft(h, M);
+    double *hf = t64 + 4 * M, *hi = t64 + 6 * M;
+    for (int64_t k = 0; k < M; ++k) {
+      const std::complex<long double> v = h[k] / static_cast<long double>(M);
+      const std::complex<long double> w = std::conj(h[(M - k) % M]) / static_cast<long double>(M);
+      hf[2 * k] = static_cast<double>(v.real());
+      hf[2 * k + 1] = static_cast<double>(v.imag());
+      hi[2 * k] = static_cast<double>(w.real());
+      hi[2 * k + 1] = static_cast<double>(w.imag());
+    }
+    for (int64_t i = 0; i < 2 * n64; ++i) t32[i] = static_cast<float>(t64[i]);
+    void *tab = nullptr;
+    hipError_t e = dev_alloc(p, &tab, static_cast<size_t>(n64) * 24);
+    if (e == hipSuccess) e = hipMemcpy(tab, t64, static_cast<size_t>(n64) * 16, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(static_cast<char *>(tab) + n64 * 16, t32, static_cast<size_t>(n64) * 8, hipMemcpyHostToDevice);
+    delete[] h;
+    delete[] t64;
+    delete[] t32;
+    FFTMV_TRY(e);
+    const cx64 *d64 = static_cast<const cx64 *>(tab);
+    const cx32 *d32 = reinterpret_cast<const cx32 *>(static_cast<const char *>(tab) + n64 * 16);
+    p->bt.tw64 = d64;
+    p->bt.hf64 = d64 + 2 * M;
+    p->bt.hi64 = d64 + 3 * M;
+    p->bt.tw32 = d32;
+    p->bt.hf32 = d32 + 2 * M;
+    p->bt.hi32 = d32 + 3 * M;
+    p->ws_bytes += static_cast<size_t>(n64) * 24;
+  }
+
   // stage buffers, sized for FP64 so that any precision mask fits
   for (int dir = 0; dir < 2; ++dir) {
     const int64_t ldi = padded_ld(channels_in(p, dir)), ldo = padded_ld(channels_out(p, dir));
@@ -354,7 +439,7 @@ int setup_impl(fftmv_plan_s *p, const double *F, hipStream_t s) {
   a.fstride64 = Nd * p->ldF64;
   a.ldr64 = p->ldF64;
   a.cpr = Nm;
-  FFTMV_TRY(launch_fft_forward(p->geom, a, false, p->tw64, s));
+  FFTMV_TRY(launch_fft_forward(p->geom, a, false, p->tw64, s, p->blue ? &p->bt : nullptr));
   FFTMV_TRY(hipStreamSynchronize(s));
   return FFTMV_SUCCESS;
 }
@@ -494,10 +579,19 @@ int fftmv_setup(fftmv_plan_t *out, const double *F_dev, int64_t Nm, int64_t Nd, 
     p->K = Nt + 1;
     p->prec = mask & FFTMV_PREC_BITS;
     p->flags = mask & FFTMV_FLAG_BITS;
-    if (!build_geometry(Nt, &p->geom) || fft_channels_per_block(p->geom, false, 1) == 0 ||
-        fft_channels_per_block(p->geom, true, 1) == 0) {
-      delete p;
-      return FFTMV_ERR_UNSUPPORTED_SIZE;
+    const bool radix = build_geometry(Nt, &p->geom) && fft_channels_per_block(p->geom, false, 1) > 0 &&
+                       fft_channels_per_block(p->geom, true, 1) > 0;
+    if (!radix) {
+      // lengths without a radix schedule: Bluestein form over M points
+      const int64_t M = bluestein_length(Nt);
+      if (M == 0) {
+        delete p;
+        return FFTMV_ERR_UNSUPPORTED_SIZE;
+      }
+      p->blue = true;
+      p->bt.gM = make_geometry(static_cast<int>(M));
+      p->geom = FftGeom{};
+      p->geom.L = static_cast<int>(Nt);
     }
     if (hipGetDevice(&p->device) != hipSuccess) {
       delete p;
@@ -541,7 +635,7 @@ const char *fftmv_status_string(int status) {
   switch (status) {
     case FFTMV_SUCCESS: return "success";
     case FFTMV_ERR_INVALID_ARG: return "invalid argument";
-    case FFTMV_ERR_UNSUPPORTED_SIZE: return "unsupported size (Nt must be 2^a*3^b*5^c*7^d and at most 4096)";
+    case FFTMV_ERR_UNSUPPORTED_SIZE: return "unsupported size (Nt above 4096, or above 2048 without a radix-2/3/5/7 factorisation)";
     case FFTMV_ERR_OUT_OF_MEMORY: return "out of device memory";
     case FFTMV_ERR_HIP: return "HIP runtime error";
     case FFTMV_ERR_INTERNAL: return "internal error";

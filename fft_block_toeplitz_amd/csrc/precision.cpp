@@ -45,10 +45,13 @@ double predict_error(const Problem &p, uint32_t bits, double kappa, const double
                   c[4] * unit_roundoff(bits, 5));
 }
 
+bool radix_fits(int64_t Nt);
+
 // HBM: algorithmic bytes of each kernel of one apply; a buffer between
 // stages s and s+1 holds the narrower of their precisions. LDS: each pass of
 // a batched FFT writes and reads its tile of Nt complex values per channel
-// in the precision of its stage.
+// (in Bluestein form: two transforms of M values) in the precision of its
+// stage.
 double predict_seconds(const Problem &p, uint32_t bits, bool staged, const double *c) {
   const double K = p.Nt + 1.0;
   const double nin = p.dir == 0 ? p.Nm : p.Nd, nout = p.dir == 0 ? p.Nd : p.Nm;
@@ -66,17 +69,27 @@ double predict_seconds(const Problem &p, uint32_t bits, bool staged, const doubl
     bytes = (p.Nt * nin * 8.0 + hin) + (fhat + hin + hout) + (hout + p.Nt * nout * 8.0);
     kernels = 3;
   }
-  const double passes = static_cast<double>(make_geometry(static_cast<int>(p.Nt)).npass);
-  const double lds = 2.0 * passes * p.Nt *
-                     (nin * (fp32(bits, 2) ? 8.0 : 16.0) + nout * (fp32(bits, 4) ? 8.0 : 16.0));
+  const int64_t Nt = static_cast<int64_t>(p.Nt);
+  double tile_passes = 0.0;  // passes times tile length, per channel
+  if (radix_fits(Nt)) {
+    tile_passes = make_geometry(static_cast<int>(Nt)).npass * p.Nt;
+  } else {
+    const int64_t M = fftmv::bluestein_length(Nt);
+    tile_passes = 2.0 * make_geometry(static_cast<int>(M)).npass * static_cast<double>(M);
+  }
+  const double lds = 2.0 * tile_passes * (nin * (fp32(bits, 2) ? 8.0 : 16.0) + nout * (fp32(bits, 4) ? 8.0 : 16.0));
   return bytes / c[6] + lds / c[7] + kernels * c[8];
 }
 
-// the sizes fftmv_setup accepts
-bool supported(int64_t Nt) {
-  if (Nt < 1 || Nt > 4096) return false;
+// the sizes fftmv_setup accepts: a radix schedule that fits a workgroup,
+// else the Bluestein form
+bool radix_fits(int64_t Nt) {
   const fftmv::FftGeom g = make_geometry(static_cast<int>(Nt));
   return g.L == Nt && fftmv::fft_channels_per_block(g, false, 1) > 0 && fftmv::fft_channels_per_block(g, true, 1) > 0;
+}
+bool supported(int64_t Nt) {
+  if (Nt < 1 || Nt > 4096) return false;
+  return radix_fits(Nt) || fftmv::bluestein_length(Nt) > 0;
 }
 
 bool valid(int64_t Nm, int64_t Nd, int64_t Nt, int dir, uint32_t flags, double kappa, const double *c) {

@@ -28,11 +28,14 @@
  *   d, v [Nt][Nd]
  * Pointers need 8-byte alignment (natural for double).
  *
- * Supported sizes: 1 <= Nm, Nd <= 2^31 - 1; 1 <= Nt <= 4096 with
- * Nt = 2^a 3^b 5^c 7^d (radix 2/4/8, 3, 5 and 7 passes), except the few
- * lengths whose radix-7 passes need more registers than a workgroup holds
- * (Nt > 3584 with a factor 7); any other size returns
- * FFTMV_ERR_UNSUPPORTED_SIZE.
+ * Supported sizes: 1 <= Nm, Nd <= 2^31 - 1, and 1 <= Nt <= 4096 where
+ *   - Nt = 2^a 3^b 5^c 7^d runs with radix 2/4/8, 3, 5 and 7 passes (except
+ *     the few lengths above 3584 with a factor 7, whose radix-7 passes need
+ *     more registers than a workgroup holds), and
+ *   - any other Nt <= 2048 runs in Bluestein (chirp-z) form: the length-Nt
+ *     transform as a circular convolution of a power-of-two length
+ *     M >= 2 Nt - 1;
+ * any other size returns FFTMV_ERR_UNSUPPORTED_SIZE.
  *
  * Ownership and concurrency:
  *   - fftmv_setup is synchronous: when it returns the frequency blocks are
@@ -69,7 +72,7 @@ extern "C" {
 /* ----------------------------------------------------------------- status */
 #define FFTMV_SUCCESS 0
 #define FFTMV_ERR_INVALID_ARG (-1)      /* null pointer, bad size/mask/stage  */
-#define FFTMV_ERR_UNSUPPORTED_SIZE (-2) /* Nt not 2^a 3^b 5^c 7^d, or too large */
+#define FFTMV_ERR_UNSUPPORTED_SIZE (-2) /* Nt outside the supported lengths    */
 #define FFTMV_ERR_OUT_OF_MEMORY (-3)    /* device allocation failed           */
 #define FFTMV_ERR_HIP (-4)              /* a HIP runtime call or launch failed */
 #define FFTMV_ERR_INTERNAL (-5)         /* unexpected library condition       */

@@ -60,8 +60,9 @@ FAKE = 0x10000  # never dereferenced: every case below fails validation first
     ((FAKE, 8, 0, 16, 0), fm.FFTMV_ERR_INVALID_ARG),            # Nd < 1
     ((FAKE, 8, 4, 0, 0), fm.FFTMV_ERR_INVALID_ARG),             # Nt < 1
     ((FAKE, 8, 4, 16, 1 << 12), fm.FFTMV_ERR_INVALID_ARG),      # unknown mask bit
-    ((FAKE, 8, 4, 11, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE),       # factor 11
-    ((FAKE, 8, 4, 2 * 13, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE),   # factor 13
+    ((FAKE, 8, 4, 2053, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE),     # prime above 2048: no radix schedule,
+                                                                # Bluestein tile too large
+    ((FAKE, 8, 4, 2 * 2053, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE), # the same factor
     ((FAKE, 8, 4, 3920, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE),     # 2^4 5 7^2: radix-7 passes do not fit
     ((FAKE, 8, 4, 5000, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE),     # Nt > 4096
     ((FAKE, 1 << 31, 4, 16, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE), # Nm too large

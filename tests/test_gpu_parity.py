@@ -101,6 +101,14 @@ SHAPES = [
     (3, 2, 2187),    # 3^7
     (2, 2, 3584),    # 2^9 7: the longest radix-7 length that fits
     (129, 33, 105),  # 3 5 7, wide batch (many channels per workgroup)
+    # Bluestein form (lengths with other prime factors)
+    (5, 3, 11),      # M = 32
+    (4, 2, 13),
+    (3, 3, 97),
+    (129, 33, 101),  # wide batch, M = 256
+    (6, 4, 1009),
+    (7, 5, 1001),    # 7 11 13
+    (2, 2, 2039),    # the longest prime in Bluestein form, M = 4096
 ]
 
 
@@ -125,7 +133,8 @@ def test_apply_matches_oracle(fm, shape, mask, staged):
                                    (37, 111, 1000),   # wide batch, odd rows: channel pairs straddle rows
                                    (33, 7, 2000),     # narrow batch, Nt = 2000
                                    (2048, 2, 2000),   # wide batch, Nt = 2000, 256-byte aligned rows
-                                   (9, 4, 21)])       # radix 3 and 7
+                                   (9, 4, 21),        # radix 3 and 7
+                                   (9, 4, 13)])       # Bluestein form
 def test_fhat_matches_oracle(fm, shape):
     c = case(*shape)
     Nm, Nd, Nt = shape
@@ -186,7 +195,7 @@ def test_stage_by_stage(fm, mask):
     plan.close()
 
 
-@pytest.mark.parametrize("shape", [(37, 5, 20), (37, 5, 1000), (37, 5, 63)])
+@pytest.mark.parametrize("shape", [(37, 5, 20), (37, 5, 1000), (37, 5, 63), (37, 5, 11)])
 def test_all_precision_masks(fm, shape):
     """Every one of the 32 per-stage precision choices of each direction,
     on one plan holding Fhat in both precisions."""
