@@ -88,6 +88,7 @@ SHAPES = [
     (1001, 3, 8),
     (2, 130, 40),    # Nd > Nm: tall blocks
     (129, 65, 1000), # Main's time length, ragged channel counts
+    (4103, 3, 1000), # wide batches (10-channel tiles, ragged last tile) at Main's length
     (33, 7, 2000),   # the Scale share's time length, narrow batches
     (3, 2, 4096),    # the longest supported transform, 2Nt = 2^13
     (2, 3, 3125),    # 2Nt = 2 * 5^5
