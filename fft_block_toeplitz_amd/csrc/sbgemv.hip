@@ -204,14 +204,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
 // w_k[c] = sum_r conj(Fhat_k[r][c]) d_k[r].
 // One workgroup per (frequency k, chunk of VL*256 consecutive 16-byte column
 // vectors): each lane owns VL vectors 256 apart (a vector is two complex64
-// columns or one complex128 column) and walks down all Nd rows with U rows
-// in flight, so the workgroup reads VL*4 KiB contiguous of each row per step;
-// no cross-lane reduction. The host picks VL so that a frequency splits into
-// chunks of nearly equal size. d_k[r] is the same for the whole workgroup (a
-// scalar load). Row r feeds chain (r mod U) mod S (the last Nd mod U rows
-// feed chain 0), and the S chains are added at the end.
-template <typename T, typename In, int VL, int U, int S>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void sbgemv_c_kernel(
+// columns or one complex128 column) and walks down all Nd rows, one row at a
+// time, keeping one partial sum per column: no cross-lane reduction. That
+// fits a lane in 64 VGPRs, so eight waves run per SIMD and every workgroup
+// of the Main shape (2 chunks x 1001 frequencies = 2002 workgroups on 2048
+// slots) is resident at once. Measured at Main: one row per load group at
+// eight waves per SIMD (600 us) beats two rows per group at four waves
+// (622 us), two partial sums per column at eight waves (641 us, spills) and
+// the rows split over two half-workgroups (630 us). d_k[r] is the same for
+// the whole workgroup (a scalar load, U rows per load).
+template <typename T, typename In, int VL, int U>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void sbgemv_c_kernel(
     const typename Vec16<T>::type *__restrict__ F, const cx<In> *__restrict__ x, void *__restrict__ y, int64_t Nd,
     int64_t ldF_vec, int64_t nvec, int64_t ldx, int64_t ldy, bool y_f32, int64_t nchunks, int64_t nblocks) {
   using V = typename Vec16<T>::type;
@@ -229,45 +232,36 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     off[v] = static_cast<uint32_t>(j) * static_cast<uint32_t>(sizeof(V));
   }
 
-  T ar[S][VL][NV], ai[S][VL][NV];
+  T ar[VL][NV], ai[VL][NV];
 #pragma unroll
-  for (int c = 0; c < S; ++c)
+  for (int v = 0; v < VL; ++v)
 #pragma unroll
-    for (int v = 0; v < VL; ++v)
-#pragma unroll
-      for (int e = 0; e < NV; ++e) ar[c][v][e] = ai[c][v][e] = T(0);
+    for (int e = 0; e < NV; ++e) ar[v][e] = ai[v][e] = T(0);
 
-  // Per step: the U rows of one column group are loaded together, then
-  // used; measured faster than putting all U*VL loads in flight at once
-  // (fewer distinct DRAM rows open per wave).
   int64_t r = 0;
   for (; r + U <= Nd; r += U) {
     cx<T> d[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) d[u] = cvt<T>(xk[r + u]);
 #pragma unroll
-    for (int v = 0; v < VL; ++v) {
-      V fv[U];
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int u = 0; u < U; ++u) fv[u] = load_stream_at(base + (r + u) * ldF_vec, off[v]);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int v = 0; v < VL; ++v) {
         cx<T> f[NV];
-        split(fv[u], f);
+        split(load_stream_at(base + (r + u) * ldF_vec, off[v]), f);
 #pragma unroll
-        for (int e = 0; e < NV; ++e) fma_conj_mul(ar[u % S][v][e], ai[u % S][v][e], f[e], d[u]);
+        for (int e = 0; e < NV; ++e) fma_conj_mul(ar[v][e], ai[v][e], f[e], d[u]);
+        __builtin_amdgcn_sched_barrier(0);  // one load group in flight per wave
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep the next group's loads after this group's use
-    }
   }
   for (; r < Nd; ++r) {  // fewer than U rows left
-    cx<T> d = cvt<T>(xk[r]);
+    const cx<T> d = cvt<T>(xk[r]);
 #pragma unroll
     for (int v = 0; v < VL; ++v) {
       cx<T> f[NV];
       split(load_stream_at(base + r * ldF_vec, off[v]), f);
 #pragma unroll
-      for (int e = 0; e < NV; ++e) fma_conj_mul(ar[0][v][e], ai[0][v][e], f[e], d);
+      for (int e = 0; e < NV; ++e) fma_conj_mul(ar[v][e], ai[v][e], f[e], d);
     }
   }
 
@@ -277,15 +271,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     if (j < nvec) {
       cx<T> out[NV];
 #pragma unroll
-      for (int e = 0; e < NV; ++e) {
-        T sr = ar[0][v][e], si = ai[0][v][e];
-#pragma unroll
-        for (int c = 1; c < S; ++c) {
-          sr += ar[c][v][e];
-          si += ai[c][v][e];
-        }
-        out[e] = mk(sr, si);
-      }
+      for (int e = 0; e < NV; ++e) out[e] = mk(ar[v][e], ai[v][e]);
       store_vec(y, k * ldy + j * NV, y_f32, out);
     }
   }
@@ -294,17 +280,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
 constexpr int kRowsN = 4;    // rows per wave, F direction
 constexpr int kUnrollN = 2;  // vectors per row in flight, F direction
 constexpr int kMaxVecsC = 5;  // vectors per lane, F* direction (at most)
-constexpr int kChainsC = 2;   // accumulator chains per column, F* direction
-// rows in flight, F* direction: VL*U loads stay under the register budget
-// of four waves per SIMD
-constexpr int unroll_c(int vl) { return vl >= 4 ? 2 : 4; }
+constexpr int kUnrollC = 2;   // rows per step (one scalar load of d_k), F* direction
 
 template <typename T, typename In, int VL>
 void launch_c(const SbgemvArgs &a, int64_t nvec, int64_t nchunks, hipStream_t s) {
   using V = typename Vec16<T>::type;
   const int nv = Vec16<T>::n;
   const int64_t nblocks = a.K * nchunks;
-  hipLaunchKernelGGL((sbgemv_c_kernel<T, In, VL, unroll_c(VL), kChainsC>), dim3(static_cast<unsigned>(nblocks)),
+  hipLaunchKernelGGL((sbgemv_c_kernel<T, In, VL, kUnrollC>), dim3(static_cast<unsigned>(nblocks)),
                      dim3(kBlock), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
                      a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks);
 }
