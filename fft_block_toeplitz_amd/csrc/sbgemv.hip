@@ -120,15 +120,15 @@ __device__ __forceinline__ void fma_conj_mul(T &re, T &im, cx<T> f, cx<T> x) {
 // piece of m_k is loaded once for all R rows. U vectors per row are in flight
 // per step (R*U Fhat loads issued before any arithmetic). Per-lane partial
 // sums are closed with wave_sum (DPP).
-template <typename T, typename In, int R, int U>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void sbgemv_n_kernel(const typename Vec16<T>::type *__restrict__ F,
+template <typename T, typename In, int R, int U, int NCH, int WPE>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void sbgemv_n_kernel(const typename Vec16<T>::type *__restrict__ F,
                                                           const cx<In> *__restrict__ x, void *__restrict__ y,
                                                           int64_t Nd, int64_t ldF_vec, int64_t nvec, int64_t ldx,
                                                           int64_t ldy, bool y_f32, int64_t ngroups, int64_t ntasks,
                                                           int64_t nblocks) {
   using V = typename Vec16<T>::type;
   constexpr int NV = Vec16<T>::n;
-  constexpr int NC = U * NV;  // chains per row and lane
+  constexpr int NC = U * NV < NCH ? U * NV : NCH;  // chains per row and lane
   const int lane = threadIdx.x & (kWave - 1);
   // the wave index is uniform across the wave: say so, so that the task,
   // the row pointers and the loop bounds live in scalar registers
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         cx<T> f[NV];
         split(fv[u][i], f);
 #pragma unroll
-        for (int e = 0; e < NV; ++e) fma_mul(ar[i][u * NV + e], ai[i][u * NV + e], f[e], xv[u][e]);
+        for (int e = 0; e < NV; ++e) fma_mul(ar[i][(u * NV + e) % NC], ai[i][(u * NV + e) % NC], f[e], xv[u][e]);
       }
   }
   for (; j < nvec; j += kWave) {  // fewer than U vectors left in the row
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
       cx<T> f[NV];
       split(load_stream_at(rows[i], static_cast<uint32_t>(j) * static_cast<uint32_t>(sizeof(V))), f);
 #pragma unroll
-      for (int e = 0; e < NV; ++e) fma_mul(ar[i][e], ai[i][e], f[e], xv[e]);
+      for (int e = 0; e < NV; ++e) fma_mul(ar[i][e % NC], ai[i][e % NC], f[e], xv[e]);
     }
   }
 
@@ -279,6 +279,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
 
 constexpr int kRowsN = 4;    // rows per wave, F direction
 constexpr int kUnrollN = 2;  // vectors per row in flight, F direction
+constexpr int kChainsN = 4;  // partial sums per row and lane, F direction
+constexpr int kWavesN = 4;   // waves per SIMD the registers are sized for, F direction
 constexpr int kMaxVecsC = 5;  // vectors per lane, F* direction (at most)
 constexpr int kUnrollC = 2;   // rows per step (one scalar load of d_k), F* direction
 
@@ -319,15 +321,15 @@ hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
   const dim3 grid(static_cast<unsigned>(nblocks)), block(kBlock);
   const int64_t ldF_vec = a.ldF / nv;
   if (compute_f32) {
-    hipLaunchKernelGGL((sbgemv_n_kernel<float, float, kRowsN, kUnrollN>), grid, block, 0, s,
+    hipLaunchKernelGGL((sbgemv_n_kernel<float, float, kRowsN, kUnrollN, kChainsN, kWavesN>), grid, block, 0, s,
                        static_cast<const f32x4 *>(a.F), static_cast<const cx<float> *>(a.x), a.y, a.Nd, ldF_vec,
                        nvec, a.ldx, a.ldy, a.y_f32, ngroups, ntasks, nblocks);
   } else if (a.x_f32) {
-    hipLaunchKernelGGL((sbgemv_n_kernel<double, float, kRowsN, kUnrollN>), grid, block, 0, s,
+    hipLaunchKernelGGL((sbgemv_n_kernel<double, float, kRowsN, kUnrollN, kChainsN, kWavesN>), grid, block, 0, s,
                        static_cast<const f64x2 *>(a.F), static_cast<const cx<float> *>(a.x), a.y, a.Nd, ldF_vec,
                        nvec, a.ldx, a.ldy, a.y_f32, ngroups, ntasks, nblocks);
   } else {
-    hipLaunchKernelGGL((sbgemv_n_kernel<double, double, kRowsN, kUnrollN>), grid, block, 0, s,
+    hipLaunchKernelGGL((sbgemv_n_kernel<double, double, kRowsN, kUnrollN, kChainsN, kWavesN>), grid, block, 0, s,
                        static_cast<const f64x2 *>(a.F), static_cast<const cx<double> *>(a.x), a.y, a.Nd, ldF_vec,
                        nvec, a.ldx, a.ldy, a.y_f32, ngroups, ntasks, nblocks);
   }
