@@ -162,7 +162,9 @@ __device__ __forceinline__ void ct_last_pass(const cx<T> *lds, const cx<T> *__re
 // SETUP = false: the apply path -- one output row per frequency, 32-bit
 // offsets. SETUP = true: the frequency blocks -- channel ch goes to row
 // ch / cpr, column ch % cpr of its frequency's block, 64-bit offsets.
-template <typename T, int L, int C, int TPB, bool NTS, bool ROUND, bool SETUP = false>
+// Src: the sample type (double; float for the stage-1 buffer of the
+// five-kernel form when stage 1 or 2 is FP32).
+template <typename T, int L, int C, int TPB, bool NTS, bool ROUND, bool SETUP = false, typename Src = double>
 __global__ __launch_bounds__(TPB) void rfft_forward_ct(FwdFftArgs a, const cx<T> *__restrict__ tw,
                                                        int64_t nblocks) {
   constexpr FftGeom g = make_geometry(L);
@@ -172,14 +174,14 @@ __global__ __launch_bounds__(TPB) void rfft_forward_ct(FwdFftArgs a, const cx<T>
   const int64_t tile = xcd_contiguous_block(blockIdx.x, nblocks);
   const int64_t ch = tile * C + c;
   const bool live = ch < a.nchan;
-  const double *src = static_cast<const double *>(a.src);
+  const Src *src = static_cast<const Src *>(a.src);
   const int64_t ld = a.src_ld;
   auto get = [&](int n) {
     const int t0 = 2 * n;  // t0 < L = Nt is guaranteed for n < NZ, L even or odd
     T re = T(0), im = T(0);
     if (live) {
-      double x0 = load_elem<!SETUP>(src, t0 * ld + ch), x1 = 0.0;
-      if (t0 + 1 < L) x1 = load_elem<!SETUP>(src, (t0 + 1) * ld + ch);
+      double x0 = static_cast<double>(load_elem<!SETUP>(src, t0 * ld + ch)), x1 = 0.0;
+      if (t0 + 1 < L) x1 = static_cast<double>(load_elem<!SETUP>(src, (t0 + 1) * ld + ch));
       if constexpr (ROUND) {
         x0 = round_f32(x0);
         x1 = round_f32(x1);
@@ -321,20 +323,20 @@ constexpr CtTile ct_wide_tile(int L) {
 constexpr bool has_ct(int L) { return L == 1000 || L == 2000; }
 constexpr int64_t kWideBatch = 4096;  // channels from which wide tiles pay
 
-template <typename T, int L, bool ROUND, int C, int TPB = kBlock>
+template <typename T, int L, bool ROUND, typename Src, int C, int TPB = kBlock>
 void launch_fwd_ct(const FwdFftArgs &a, const void *tw, hipStream_t s) {
   const int64_t nblocks = (a.nchan + C - 1) / C;
-  hipLaunchKernelGGL((rfft_forward_ct<T, L, C, TPB, true, ROUND>), dim3(static_cast<unsigned>(nblocks)), dim3(TPB),
-                     0, s, a, static_cast<const cx<T> *>(tw), nblocks);
+  hipLaunchKernelGGL((rfft_forward_ct<T, L, C, TPB, true, ROUND, false, Src>), dim3(static_cast<unsigned>(nblocks)),
+                     dim3(TPB), 0, s, a, static_cast<const cx<T> *>(tw), nblocks);
 }
 
-template <typename T, int L, bool ROUND>
+template <typename T, int L, bool ROUND, typename Src = double>
 void launch_fwd_ct_c(const FwdFftArgs &a, const void *tw, hipStream_t s) {
   constexpr CtTile w = ct_wide_tile<T>(L);
   if (a.nchan >= kWideBatch)
-    launch_fwd_ct<T, L, ROUND, w.C, w.tpb>(a, tw, s);
+    launch_fwd_ct<T, L, ROUND, Src, w.C, w.tpb>(a, tw, s);
   else
-    launch_fwd_ct<T, L, ROUND, 1>(a, tw, s);
+    launch_fwd_ct<T, L, ROUND, Src, 1>(a, tw, s);
 }
 
 // the frequency blocks (setup): FP64 transform, 64-bit offsets, rows of cpr
@@ -359,6 +361,13 @@ void launch_fwd_ct_setup(const FwdFftArgs &a, const void *tw, hipStream_t s) {
 
 template <int L>
 void launch_fwd_ct_any(const FwdFftArgs &a, bool compute_f32, const void *tw, hipStream_t s) {
+  if (a.src_f32) {  // the stage-1 buffer of the five-kernel form (already rounded)
+    if (compute_f32)
+      launch_fwd_ct_c<float, L, false, float>(a, tw, s);
+    else
+      launch_fwd_ct_c<double, L, false, float>(a, tw, s);
+    return;
+  }
   if (compute_f32)
     launch_fwd_ct_c<float, L, false>(a, tw, s);  // conversion to float rounds
   else if (a.round_f32)
@@ -370,8 +379,8 @@ void launch_fwd_ct_any(const FwdFftArgs &a, bool compute_f32, const void *tw, hi
 // the specialised forward kernel covers the apply path: FP64 input, one
 // output row per frequency, byte offsets below 4 GiB
 bool fwd_ct_applies(const FftGeom &g, const FwdFftArgs &a) {
-  return has_ct(g.L) && a.Nt == g.L && !a.src_f32 && a.cpr >= a.nchan && fits_32bit(a.Nt, a.src_ld, 8) &&
-         a.nchan <= a.src_ld;
+  return has_ct(g.L) && a.Nt == g.L && !(a.src_f32 && a.round_f32) && a.cpr >= a.nchan &&
+         fits_32bit(a.Nt, a.src_ld, 8) && a.nchan <= a.src_ld;
 }
 
 template <typename T, typename Src, int L, int C, int TPB = kBlock>

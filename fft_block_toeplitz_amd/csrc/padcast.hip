@@ -11,34 +11,66 @@
 namespace fftmv {
 namespace {
 
-// One workgroup row-segment of 256 consecutive columns per (blockIdx.x,
-// blockIdx.y): consecutive lanes touch consecutive addresses on both sides.
-template <typename S, typename D>
+// Each thread copies V consecutive columns (one 16-byte load of double
+// pairs, or an 8-byte load of float pairs, when V = 2) of kRowsPerBlock
+// rows; consecutive lanes touch consecutive addresses on both sides.
+constexpr int kRowsPerBlock = 4;
+
+template <typename S, typename D, int V>
 __global__ __launch_bounds__(kBlock) void cast_kernel(const S *__restrict__ src, int64_t lds, D *__restrict__ dst,
                                                       int64_t ldd, int64_t rows, int64_t cols) {
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  const int64_t c = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) * V;
   if (c >= cols) return;
-  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) dst[r * ldd + c] = static_cast<D>(src[r * lds + c]);
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kRowsPerBlock;
+  const int64_t r1 = r0 + kRowsPerBlock < rows ? r0 + kRowsPerBlock : rows;
+  if constexpr (V == 2) {
+    typedef S S2 __attribute__((ext_vector_type(2)));
+    typedef D D2 __attribute__((ext_vector_type(2)));
+    if (c + 1 < cols) {
+      S2 in[kRowsPerBlock];
+#pragma unroll
+      for (int i = 0; i < kRowsPerBlock; ++i)
+        if (r0 + i < r1) in[i] = *reinterpret_cast<const S2 *>(src + (r0 + i) * lds + c);
+#pragma unroll
+      for (int i = 0; i < kRowsPerBlock; ++i)
+        if (r0 + i < r1)
+          *reinterpret_cast<D2 *>(dst + (r0 + i) * ldd + c) = D2{static_cast<D>(in[i].x), static_cast<D>(in[i].y)};
+      return;
+    }
+  }
+  for (int64_t r = r0; r < r1; ++r) dst[r * ldd + c] = static_cast<D>(src[r * lds + c]);  // last odd column
+}
+
+template <typename S, typename D>
+void cast(const CastArgs &a, hipStream_t s) {
+  // pairs when both row strides are even and both bases are aligned to a pair
+  const bool pairs = (a.lds % 2 == 0) && (a.ldd % 2 == 0) && (reinterpret_cast<uintptr_t>(a.src) % (2 * sizeof(S)) == 0) &&
+                     (reinterpret_cast<uintptr_t>(a.dst) % (2 * sizeof(D)) == 0);
+  const int v = pairs ? 2 : 1;
+  const int64_t per = static_cast<int64_t>(kBlock) * v;
+  const dim3 grid(static_cast<unsigned>((a.cols + per - 1) / per),
+                  static_cast<unsigned>((a.rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  if (pairs)
+    hipLaunchKernelGGL((cast_kernel<S, D, 2>), grid, dim3(kBlock), 0, s, static_cast<const S *>(a.src), a.lds,
+                       static_cast<D *>(a.dst), a.ldd, a.rows, a.cols);
+  else
+    hipLaunchKernelGGL((cast_kernel<S, D, 1>), grid, dim3(kBlock), 0, s, static_cast<const S *>(a.src), a.lds,
+                       static_cast<D *>(a.dst), a.ldd, a.rows, a.cols);
 }
 
 }  // namespace
 
 hipError_t launch_cast(const CastArgs &a, hipStream_t s) {
   if (a.rows <= 0 || a.cols <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((a.cols + kBlock - 1) / kBlock),
-                  static_cast<unsigned>(a.rows < 65535 ? a.rows : 65535));
+  if ((a.rows + kRowsPerBlock - 1) / kRowsPerBlock > 65535) return hipErrorInvalidValue;
   if (a.src_f32 && a.dst_f32)
-    hipLaunchKernelGGL((cast_kernel<float, float>), grid, dim3(kBlock), 0, s, static_cast<const float *>(a.src), a.lds,
-                       static_cast<float *>(a.dst), a.ldd, a.rows, a.cols);
+    cast<float, float>(a, s);
   else if (a.src_f32)
-    hipLaunchKernelGGL((cast_kernel<float, double>), grid, dim3(kBlock), 0, s, static_cast<const float *>(a.src),
-                       a.lds, static_cast<double *>(a.dst), a.ldd, a.rows, a.cols);
+    cast<float, double>(a, s);
   else if (a.dst_f32)
-    hipLaunchKernelGGL((cast_kernel<double, float>), grid, dim3(kBlock), 0, s, static_cast<const double *>(a.src),
-                       a.lds, static_cast<float *>(a.dst), a.ldd, a.rows, a.cols);
+    cast<double, float>(a, s);
   else
-    hipLaunchKernelGGL((cast_kernel<double, double>), grid, dim3(kBlock), 0, s, static_cast<const double *>(a.src),
-                       a.lds, static_cast<double *>(a.dst), a.ldd, a.rows, a.cols);
+    cast<double, double>(a, s);
   return hipGetLastError();
 }
 

@@ -196,12 +196,14 @@ def test_stage_by_stage(fm, mask):
     plan.close()
 
 
-@pytest.mark.parametrize("shape", [(37, 5, 20), (37, 5, 1000), (37, 5, 63), (37, 5, 11)])
-def test_all_precision_masks(fm, shape):
+@pytest.mark.parametrize("shape,staged", [((37, 5, 20), False), ((37, 5, 1000), False), ((37, 5, 63), False),
+                                          ((37, 5, 11), False), ((37, 5, 1000), True), ((4103, 3, 1000), True)])
+def test_all_precision_masks(fm, shape, staged):
     """Every one of the 32 per-stage precision choices of each direction,
-    on one plan holding Fhat in both precisions."""
+    on one plan holding Fhat in both precisions (fused, or the five-kernel
+    form with its stage buffers in every precision combination)."""
     c = case(*shape)
-    plan = fm.Plan(c.F_dev, fm.FFTMV_FLAG_FHAT_BOTH)
+    plan = fm.Plan(c.F_dev, fm.FFTMV_FLAG_FHAT_BOTH | (fm.FFTMV_FLAG_STAGED if staged else 0))
     worst = {}
     for direction in (0, 1):
         for bits in range(32):
