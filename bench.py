@@ -64,6 +64,7 @@ def parse():
     ap.add_argument("--staged", action="store_true", help="five-kernel form (pad/unpad materialised)")
     ap.add_argument("--kernel-reps", type=int, default=20, help="stage-3-only launches timed for the roofline")
     ap.add_argument("--setup-reps", type=int, default=3, help="extra plan setups timed after the first")
+    ap.add_argument("--graph-steps", type=int, default=100, help="steps replayed from a HIP graph (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-cols", type=int, default=0, help="oracle sample: input columns (0 = Nm/5)")
     ap.add_argument("--no-check", action="store_true", help="skip the spot-step check against the oracle")
@@ -227,6 +228,32 @@ def main():
     ms_step = total_ms / args.steps
     print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f}s)", file=sys.stderr, flush=True)
 
+    # the same step replayed from a HIP graph (context: launch overhead)
+    graph_ms = None
+    if args.graph_steps:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            plan.apply(m_dev, out=v_dev)
+            plan.apply_adjoint(d_dev, out=w_dev)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            plan.apply(m_dev, out=v_dev)
+            plan.apply_adjoint(d_dev, out=w_dev)
+        for _ in range(10):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.graph_steps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.graph_steps
+        del graph
+
     bF, bA = apply_bytes(Nm, Nd, Nt, mask, 0), apply_bytes(Nm, Nd, Nt, mask, 1)
     value = (bF + bA) / (ms_step * 1e-3) / 1e9
 
@@ -320,6 +347,7 @@ def main():
         "cpu_baseline": cpu,
         "check": check,
         "context": {"page_mi355x_f_apply_ms": {"fp64": 1.9, "mixed": 1.3}},
+        "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
         "setup_s": round(setup_s, 3),
         "setup_ms": {"first": round(setup_s * 1e3, 2), "repeats": [round(x, 2) for x in setup_ms]},
     }
