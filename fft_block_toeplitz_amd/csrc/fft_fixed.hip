@@ -312,13 +312,17 @@ __global__ __launch_bounds__(TPB) void rfft_inverse_ct(InvFftArgs a, const cx<T>
 // threads for the C*L/R butterflies of a pass. Measured at Nt = 1000,
 // FP32, 5000 channels: 8 channels x 512 threads beat 4 x 256 (forward
 // 25 us vs 47 us; the 32-byte runs of the narrower tile double the bytes
-// the non-temporal stores write) and 16 x 1024.
+// the non-temporal stores write), 16 x 1024 and 10 unpadded x 640 (which
+// fits the batch in one round but loses more to its 80-byte runs); 8 x 1024
+// (one butterfly per thread and pass, two workgroups per CU) saves another
+// ~2 us per transform over 8 x 512.
 struct CtTile {
   int C, tpb;
 };
 template <typename T>
 constexpr CtTile ct_wide_tile(int L) {
-  return L == 1000 ? CtTile{sizeof(T) == 4 ? 8 : 4, 512} : CtTile{sizeof(T) == 4 ? 8 : 4, 1024};
+  return L == 1000 ? CtTile{sizeof(T) == 4 ? 8 : 4, sizeof(T) == 4 ? 1024 : 512}
+                   : CtTile{sizeof(T) == 4 ? 8 : 4, 1024};
 }
 constexpr bool has_ct(int L) { return L == 1000 || L == 2000; }
 constexpr int64_t kWideBatch = 4096;  // channels from which wide tiles pay
