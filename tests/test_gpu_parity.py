@@ -321,3 +321,22 @@ def test_applies_replay_from_a_graph(fm, shape, mask):
     note(f"graph replay {shape} mask={mask:#x}: 3 replays bitwise equal to eager")
     del g
     plan.close()
+
+
+@pytest.mark.parametrize("mask", [0x000, 0x186])
+def test_nan_input_propagates(fm, mask):
+    """Non-finite inputs are not masked: a NaN in one sample of one channel
+    reaches every frequency of that channel through the FFT, hence every
+    output of the apply (no error code)."""
+    c = case(37, 5, 20)
+    plan = fm.Plan(c.F_dev, mask)
+    m = c.m.copy()
+    m[7, 3] = np.nan
+    v = host(plan.apply(dev(m)))
+    d = c.d.copy()
+    d[11, 2] = np.nan
+    w = host(plan.apply_adjoint(dev(d)))
+    assert np.isnan(v).all() and np.isnan(w).all()
+    # and the plan is unharmed: the next finite apply is exact again
+    assert oracle.rel_l2(host(plan.apply(c.m_dev)), c.v) <= tol(mask, 0)
+    plan.close()
