@@ -10,10 +10,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfftmv.so")
 SOURCES = [os.path.join(HERE, "csrc", f)
-           for f in ("fft.hip", "fft_fixed.hip", "sbgemv.hip", "padcast.hip", "condition.hip", "plan.cpp",
-                     "precision.cpp")]
+           for f in ("fft_generic_fwd.hip", "fft_generic_inv.hip", "fft_generic_fwd_blue.hip",
+                     "fft_generic_inv_blue.hip", "fft_fixed_fwd.hip", "fft_fixed_inv.hip", "sbgemv.hip",
+                     "padcast.hip", "condition.hip", "plan.cpp", "precision.cpp")]
 HEADERS = [os.path.join(ROOT, "include", "fftmv.h")] + [
-    os.path.join(HERE, "csrc", f) for f in ("common.hpp", "internal.hpp", "fft_device.hpp")]
+    os.path.join(HERE, "csrc", f) for f in ("common.hpp", "internal.hpp", "fft_device.hpp", "fft_fixed.hpp",
+                                            "fft_generic.hpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

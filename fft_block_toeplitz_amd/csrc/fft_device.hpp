@@ -1,5 +1,5 @@
 // Device code shared by the FFT kernels of this library (generic-length
-// kernels in fft.hip, fixed-length kernels in fft_fixed.hip): the radix
+// kernels in fft_generic.hpp, fixed-length kernels in fft_fixed.hpp): the radix
 // butterflies, twiddle application and memory helpers.
 #pragma once
 

@@ -24,6 +24,8 @@
 // stores straight to global memory, so the data cross LDS only between
 // passes. Channel tiles are numbered XCD-contiguously so that neighbouring
 // tiles, which share cache lines, share an L2.
+#pragma once
+
 #include "fft_device.hpp"
 
 namespace fftmv {
@@ -373,34 +375,6 @@ __global__ __launch_bounds__(kBlock) void rfft_inverse_kernel(FftGeom g, InvFftA
   const int pl = g.npass - 1;
   last_pass_any<T, +1, VMAX>(g.radix[pl], lds, L, logC, g.twstep[pl], tw, put);
 }
-}  // namespace
-
-// Channels per workgroup for a schedule, precision and batch: the widest C
-// that still gives at least 1024 workgroups (four per CU); for small batches
-// the narrowest C (most workgroups). C = 0 when the transform does not fit.
-FftLaunch fft_launch_config(const FftGeom &g, bool f32, int64_t nchan) {
-  const int64_t esz = f32 ? 8 : 16;
-  auto fits = [&](int C) {
-    if (static_cast<int64_t>(g.L) * C * esz > kMaxLds) return false;
-    for (int p = 0; p < g.npass; ++p) {
-      const int64_t nb = static_cast<int64_t>(g.L / g.radix[p]) * C;
-      if (nb > static_cast<int64_t>(kVmax / g.radix[p]) * kBlock) return false;
-    }
-    return true;
-  };
-  FftLaunch narrowest;
-  for (int C = kMaxChannelsPerBlock; C >= 1; C >>= 1) {
-    if (!fits(C)) continue;
-    if ((nchan + C - 1) / C >= 1024) return {C, kVmax};
-    narrowest = {C, kVmax};
-  }
-  return narrowest;
-}
-
-int fft_channels_per_block(const FftGeom &g, bool f32, int64_t nchan) { return fft_launch_config(g, f32, nchan).C; }
-
-namespace {
-
 
 int ilog2(int c) {
   int l = 0;
@@ -408,92 +382,77 @@ int ilog2(int c) {
   return l;
 }
 
-// g: the tile's schedule (length L, or M in Bluestein form); twM, hM: the
-// Bluestein tables (null otherwise)
-template <typename T, typename Src, bool ROUND>
-void fwd(const FftGeom &g, const FwdFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
+// Launch one batched transform with the generic kernels. tile: the
+// schedule of the LDS tile (length L, or M in Bluestein form); twM, hM: the
+// Bluestein tables (BLUE only).
+template <typename T, typename Src, bool ROUND, bool BLUE>
+void fwd(const FftGeom &tile, const FwdFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
          const void *hM, hipStream_t s) {
   const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
-  const size_t lds = static_cast<size_t>(g.L) * cfg.C * sizeof(cx<T>);
-  const cx<T> *t = static_cast<const cx<T> *>(tw), *tm = static_cast<const cx<T> *>(twM),
-              *h = static_cast<const cx<T> *>(hM);
-  if (hM)
-    hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmax, false, true>), dim3(static_cast<unsigned>(nblocks)),
-                       dim3(kBlock), lds, s, g, a, ilog2(cfg.C), t, nblocks, tm, h);
-  else
-    hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmax, false, false>),
-                       dim3(static_cast<unsigned>(nblocks)), dim3(kBlock), lds, s, g, a, ilog2(cfg.C), t, nblocks,
-                       tm, h);
+  const size_t lds = static_cast<size_t>(tile.L) * cfg.C * sizeof(cx<T>);
+  hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmax, false, BLUE>), dim3(static_cast<unsigned>(nblocks)),
+                     dim3(kBlock), lds, s, tile, a, ilog2(cfg.C), static_cast<const cx<T> *>(tw), nblocks,
+                     static_cast<const cx<T> *>(twM), static_cast<const cx<T> *>(hM));
 }
 
-template <typename T, typename Src>
-void inv(const FftGeom &g, const InvFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
+template <typename T, typename Src, bool BLUE>
+void inv(const FftGeom &tile, const InvFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
          const void *hM, hipStream_t s) {
   const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
-  const size_t lds = static_cast<size_t>(g.L) * cfg.C * sizeof(cx<T>);
-  const cx<T> *t = static_cast<const cx<T> *>(tw), *tm = static_cast<const cx<T> *>(twM),
-              *h = static_cast<const cx<T> *>(hM);
-  const T inv_l = T(1) / static_cast<T>(a.Nt);
-  if (hM)
-    hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmax, false, true>), dim3(static_cast<unsigned>(nblocks)),
-                       dim3(kBlock), lds, s, g, a, ilog2(cfg.C), t, inv_l, nblocks, tm, h);
-  else
-    hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmax, false, false>), dim3(static_cast<unsigned>(nblocks)),
-                       dim3(kBlock), lds, s, g, a, ilog2(cfg.C), t, inv_l, nblocks, tm, h);
+  const size_t lds = static_cast<size_t>(tile.L) * cfg.C * sizeof(cx<T>);
+  hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmax, false, BLUE>), dim3(static_cast<unsigned>(nblocks)),
+                     dim3(kBlock), lds, s, tile, a, ilog2(cfg.C), static_cast<const cx<T> *>(tw),
+                     T(1) / static_cast<T>(a.Nt), nblocks, static_cast<const cx<T> *>(twM),
+                     static_cast<const cx<T> *>(hM));
+}
+
+// the element types of one launch
+template <bool BLUE>
+void fwd_any(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg, const void *tw,
+             const void *twM, const void *hM, hipStream_t s) {
+  if (compute_f32) {
+    if (a.src_f32)
+      fwd<float, float, false, BLUE>(tile, a, cfg, tw, twM, hM, s);
+    else
+      fwd<float, double, false, BLUE>(tile, a, cfg, tw, twM, hM, s);
+  } else {
+    if (a.src_f32)
+      fwd<double, float, false, BLUE>(tile, a, cfg, tw, twM, hM, s);
+    else if (a.round_f32)
+      fwd<double, double, true, BLUE>(tile, a, cfg, tw, twM, hM, s);
+    else
+      fwd<double, double, false, BLUE>(tile, a, cfg, tw, twM, hM, s);
+  }
+}
+
+template <bool BLUE>
+void inv_any(const FftGeom &tile, const InvFftArgs &a, bool compute_f32, const FftLaunch &cfg, const void *tw,
+             const void *twM, const void *hM, hipStream_t s) {
+  if (compute_f32) {
+    if (a.src_f32)
+      inv<float, float, BLUE>(tile, a, cfg, tw, twM, hM, s);
+    else
+      inv<float, double, BLUE>(tile, a, cfg, tw, twM, hM, s);
+  } else {
+    if (a.src_f32)
+      inv<double, float, BLUE>(tile, a, cfg, tw, twM, hM, s);
+    else
+      inv<double, double, BLUE>(tile, a, cfg, tw, twM, hM, s);
+  }
 }
 
 }  // namespace
-hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
-                              hipStream_t s, const BlueTables *blue) {
-  if (!blue && launch_fft_forward_fixed(g, a, compute_f32, tw, s)) return hipGetLastError();
-  const FftGeom &tile = blue ? blue->gM : g;
-  const void *twM = blue ? (compute_f32 ? blue->tw32 : blue->tw64) : nullptr;
-  const void *hM = blue ? (compute_f32 ? blue->hf32 : blue->hf64) : nullptr;
-  const FftLaunch cfg = fft_launch_config(tile, compute_f32, a.nchan);
-  if (cfg.C == 0 || (a.nchan + cfg.C - 1) / cfg.C > INT32_MAX || (blue && !hM)) return hipErrorInvalidValue;
-  if (compute_f32) {
-    if (a.src_f32)
-      fwd<float, float, false>(tile, a, cfg, tw, twM, hM, s);
-    else
-      fwd<float, double, false>(tile, a, cfg, tw, twM, hM, s);
-  } else {
-    if (a.src_f32)
-      fwd<double, float, false>(tile, a, cfg, tw, twM, hM, s);
-    else if (a.round_f32)
-      fwd<double, double, true>(tile, a, cfg, tw, twM, hM, s);
-    else
-      fwd<double, double, false>(tile, a, cfg, tw, twM, hM, s);
-  }
-  return hipGetLastError();
-}
-hipError_t launch_fft_inverse(const FftGeom &g, const InvFftArgs &a, bool compute_f32, const void *tw,
-                              hipStream_t s, const BlueTables *blue) {
-  if (!blue && launch_fft_inverse_fixed(g, a, compute_f32, tw, s)) return hipGetLastError();
-  const FftGeom &tile = blue ? blue->gM : g;
-  const void *twM = blue ? (compute_f32 ? blue->tw32 : blue->tw64) : nullptr;
-  const void *hM = blue ? (compute_f32 ? blue->hi32 : blue->hi64) : nullptr;
-  const FftLaunch cfg = fft_launch_config(tile, compute_f32, a.nchan);
-  if (cfg.C == 0 || (a.nchan + cfg.C - 1) / cfg.C > INT32_MAX || (blue && !hM)) return hipErrorInvalidValue;
-  if (compute_f32) {
-    if (a.src_f32)
-      inv<float, float>(tile, a, cfg, tw, twM, hM, s);
-    else
-      inv<float, double>(tile, a, cfg, tw, twM, hM, s);
-  } else {
-    if (a.src_f32)
-      inv<double, float>(tile, a, cfg, tw, twM, hM, s);
-    else
-      inv<double, double>(tile, a, cfg, tw, twM, hM, s);
-  }
-  return hipGetLastError();
-}
 
-int64_t bluestein_length(int64_t L) {
-  if (L < 2 || L > (int64_t(1) << 20) || make_geometry(static_cast<int>(L)).L == L) return 0;
-  int64_t M = 1;
-  while (M < 2 * L - 1) M *= 2;
-  const FftGeom gM = make_geometry(static_cast<int>(M));
-  if (fft_channels_per_block(gM, false, 1) == 0 || fft_channels_per_block(gM, true, 1) == 0) return 0;
-  return M;
-}
+// Generic launches, one translation unit each (fft_generic_*.hip) so that
+// they compile in parallel; the Bluestein ones take the M-point tables.
+void generic_forward(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+                     const void *tw, hipStream_t s);
+void generic_forward_blue(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+                          const void *tw, const void *twM, const void *hM, hipStream_t s);
+void generic_inverse(const FftGeom &tile, const InvFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+                     const void *tw, hipStream_t s);
+void generic_inverse_blue(const FftGeom &tile, const InvFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+                          const void *tw, const void *twM, const void *hM, hipStream_t s);
+
 }  // namespace fftmv
+

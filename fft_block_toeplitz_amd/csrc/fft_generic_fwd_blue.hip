@@ -1,0 +1,12 @@
+// Generic forward batched real FFT in Bluestein (chirp-z) form, for lengths
+// without a radix schedule (see fft_generic.hpp).
+#include "fft_generic.hpp"
+
+namespace fftmv {
+
+void generic_forward_blue(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+                          const void *tw, const void *twM, const void *hM, hipStream_t s) {
+  fwd_any<true>(tile, a, compute_f32, cfg, tw, twM, hM, s);
+}
+
+}  // namespace fftmv

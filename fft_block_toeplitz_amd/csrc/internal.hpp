@@ -148,7 +148,7 @@ hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool comput
                               hipStream_t s, const BlueTables *blue = nullptr);
 hipError_t launch_fft_inverse(const FftGeom &g, const InvFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s, const BlueTables *blue = nullptr);
-// Fixed-length kernels (fft_fixed.hip): launch and return true when one
+// Fixed-length kernels (fft_fixed_fwd.hip, fft_fixed_inv.hip): launch and return true when one
 // covers this transform, else return false and launch nothing.
 bool launch_fft_forward_fixed(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s);
