@@ -129,8 +129,8 @@ def host_info():
 def cpu_baseline(shape, mask, F, m, d, cols):
     """The FP64 CPU oracle (as it stands) on a column sample of the same
     workload: Nm reduced to `cols`, everything else unchanged. One F and one
-    F* apply with Fhat precomputed, median of 3, on all the threads the
-    oracle uses and again on one thread; scaled to the full step by the byte
+    F* apply with Fhat precomputed, median of 5 on all the threads the
+    oracle uses and of 3 on one thread; scaled to the full step by the byte
     model."""
     import oracle
 
@@ -150,16 +150,16 @@ def cpu_baseline(shape, mask, F, m, d, cols):
         return float(np.median(times))
 
     threads = oracle.num_threads()
-    t = timed(3)
+    t = timed(5)
     oracle.set_num_threads(1)
     try:
-        t1 = timed(1)
+        t1 = timed(3)
     finally:
         oracle.set_num_threads(threads)
     gbs = sample_bytes / t / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"F and F* apply at Nm={cols} (of {Nm}), Nd={Nd}, Nt={Nt}, FP64 oracle, Fhat precomputed, "
-                      f"median of 3: {t * 1e3:.1f} ms; GB/s on the step's byte model at that Nm",
+                      f"median of 5: {t * 1e3:.1f} ms; GB/s on the step's byte model at that Nm",
             "ms_per_step_full_equiv": round(t * 1e3 * Nm / cols, 1),
             "one_thread": {"value": round(sample_bytes / t1 / 1e9, 3), "unit": "GB/s",
                            "ms_per_step_full_equiv": round(t1 * 1e3 * Nm / cols, 1)},

@@ -152,51 +152,50 @@ def test_fhat_matches_oracle(fm, shape):
     plan.close()
 
 
+def _inject(plan, which, rows_valid, value):
+    """Overwrite plan buffer `which` with `value` in its first columns (the
+    rest zero)."""
+    rows, ld = plan.buffer_info(which)[:2]
+    inj = np.zeros((rows, ld), np.complex128 if np.iscomplexobj(value) else np.float64)
+    inj[:, :rows_valid] = value
+    plan.write_buffer(which, dev(inj))
+
+
+@pytest.mark.parametrize("shape", [(500, 20, 256), (129, 65, 1000), (37, 5, 11)])
 @pytest.mark.parametrize("mask", [0x000, 0x186])
-def test_stage_by_stage(fm, mask):
-    """Each stage kernel fed the oracle's own input for that stage."""
-    c = case(500, 20, 256)
-    Nm, Nd, Nt = 500, 20, 256
-    K = Nt + 1
+def test_stage_by_stage(fm, shape, mask):
+    """Each stage kernel of both directions fed the oracle's own input for
+    that stage: forward FFT against the oracle's spectrum, SBGEMV against
+    its product spectrum, inverse FFT + unpad against its output (radix,
+    fixed-length and Bluestein lengths)."""
+    c = case(*shape)
+    Nm, Nd, Nt = shape
     plan = fm.Plan(c.F_dev, mask)
-    t = tol(mask, 0)
-    # stage 1 + 2: forward FFT of m against the oracle's mhat
-    plan.run_stages(0, 1, 2, x=c.m_dev)
-    mh = host(plan.read_buffer(12))[:, :Nm]
-    assert oracle.rel_l2(mh, c.mh) <= t
-    # stage 3 alone, on the oracle's mhat
-    ld = plan.buffer_info(12)[1]
-    inj = np.zeros((K, ld), np.complex128)
-    inj[:, :Nm] = c.mh
-    plan.write_buffer(12, dev(inj))
-    plan.run_stages(0, 3, 3)
-    vh = host(plan.read_buffer(13))[:, :Nd]
-    e3 = oracle.rel_l2(vh, c.vh)
-    note(f"stage 3 (F) mask={mask:#x}: {e3:.3e}")
-    assert e3 <= t
-    # stages 4 + 5 on the oracle's vhat
-    ld = plan.buffer_info(13)[1]
-    inj = np.zeros((K, ld), np.complex128)
-    inj[:, :Nd] = c.vh
-    plan.write_buffer(13, dev(inj))
-    out = torch.empty((Nt, Nd), dtype=torch.float64, device="cuda")
-    plan.run_stages(0, 4, 5, out=out)
-    assert oracle.rel_l2(host(out), c.v) <= t
-    # adjoint: stage 3 alone on the oracle's dhat
-    t = tol(mask, 1)
-    ld = plan.buffer_info(22)[1]
-    inj = np.zeros((K, ld), np.complex128)
-    inj[:, :Nd] = c.dh
-    plan.write_buffer(22, dev(inj))
-    plan.run_stages(1, 3, 3)
-    wh = host(plan.read_buffer(23))[:, :Nm]
-    e3 = oracle.rel_l2(wh, c.wh)
-    note(f"stage 3 (F*) mask={mask:#x}: {e3:.3e}")
-    assert e3 <= t
+    for direction in (0, 1):
+        t = tol(mask, direction)
+        nin, nout = (Nm, Nd) if direction == 0 else (Nd, Nm)
+        x, xh, yh, y = (c.m_dev, c.mh, c.vh, c.v) if direction == 0 else (c.d_dev, c.dh, c.wh, c.w)
+        base = 10 + 10 * direction
+        # stages 1 + 2: forward FFT of the input
+        plan.run_stages(direction, 1, 2, x=x)
+        got = host(plan.read_buffer(base + 2))[:, :nin]
+        e2 = oracle.rel_l2(got, xh)
+        # stage 3 alone, on the oracle's spectrum
+        _inject(plan, base + 2, nin, xh)
+        plan.run_stages(direction, 3, 3)
+        e3 = oracle.rel_l2(host(plan.read_buffer(base + 3))[:, :nout], yh)
+        # stages 4 + 5 on the oracle's product spectrum
+        _inject(plan, base + 3, nout, yh)
+        out = torch.empty((Nt, nout), dtype=torch.float64, device="cuda")
+        plan.run_stages(direction, 4, 5, out=out)
+        e45 = oracle.rel_l2(host(out), y)
+        note(f"stages {shape} mask={mask:#x} dir={direction}: S1+S2 {e2:.2e} S3 {e3:.2e} S4+S5 {e45:.2e}")
+        assert e2 <= t and e3 <= t and e45 <= t
     plan.close()
 
 
-@pytest.mark.parametrize("shape,staged", [((37, 5, 20), False), ((37, 5, 1000), False), ((37, 5, 63), False),
+@pytest.mark.parametrize("shape,staged", [((500, 20, 256), False), ((37, 5, 20), False), ((37, 5, 1000), False),
+                                          ((37, 5, 63), False),
                                           ((37, 5, 11), False), ((37, 5, 1000), True), ((4103, 3, 1000), True)])
 def test_all_precision_masks(fm, shape, staged):
     """Every one of the 32 per-stage precision choices of each direction,
