@@ -339,3 +339,28 @@ def test_nan_input_propagates(fm, mask):
     # and the plan is unharmed: the next finite apply is exact again
     assert oracle.rel_l2(host(plan.apply(c.m_dev)), c.v) <= tol(mask, 0)
     plan.close()
+
+
+def test_two_plans_on_two_streams(fm):
+    """Distinct plans are independent: applies of two plans issued on two
+    streams (default priority) and left to overlap give the same results as
+    when run alone."""
+    a, b = case(500, 20, 256), case(129, 65, 1000)
+    pa, pb = fm.Plan(a.F_dev, 0x186), fm.Plan(b.F_dev, 0x000)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    torch.cuda.synchronize()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            va = pa.apply(a.m_dev, stream=s1)
+            wa = pa.apply_adjoint(a.d_dev, stream=s1)
+        with torch.cuda.stream(s2):
+            vb = pb.apply(b.m_dev, stream=s2)
+            wb = pb.apply_adjoint(b.d_dev, stream=s2)
+        outs.append((va, wa, vb, wb))
+    torch.cuda.synchronize()
+    for va, wa, vb, wb in outs:
+        assert oracle.rel_l2(va.cpu().numpy(), a.v) <= TOL32 and oracle.rel_l2(wa.cpu().numpy(), a.w) <= TOL32
+        assert oracle.rel_l2(vb.cpu().numpy(), b.v) <= TOL64 and oracle.rel_l2(wb.cpu().numpy(), b.w) <= TOL64
+    pa.close()
+    pb.close()
