@@ -60,6 +60,9 @@ int64_t padded_ld(int64_t n) {
   return (n + 1) & ~int64_t(1);
 }
 
+// Largest Nm: a row of Nm complex128 entries spans at most 4 GiB.
+constexpr int64_t kMaxNm = int64_t(1) << 28;
+
 bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
 
 int status_from_hip(hipError_t e) {
@@ -569,6 +572,9 @@ int fftmv_setup(fftmv_plan_t *out, const double *F_dev, int64_t Nm, int64_t Nd, 
   if (!out || !F_dev || !aligned8(F_dev) || Nm < 1 || Nd < 1 || Nt < 1) return FFTMV_ERR_INVALID_ARG;
   if (mask & ~(FFTMV_PREC_BITS | FFTMV_FLAG_BITS)) return FFTMV_ERR_INVALID_ARG;
   if (Nm > INT32_MAX || Nd > INT32_MAX) return FFTMV_ERR_UNSUPPORTED_SIZE;
+  // the GEMV kernels address a row of Fhat with 32-bit byte offsets: a
+  // complex128 row must stay within 4 GiB
+  if (Nm > kMaxNm) return FFTMV_ERR_UNSUPPORTED_SIZE;
   if (Nt > 4096) return FFTMV_ERR_UNSUPPORTED_SIZE;
   try {
     fftmv_plan_s *p = new (std::nothrow) fftmv_plan_s();
