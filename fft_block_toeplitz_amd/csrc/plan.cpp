@@ -60,8 +60,10 @@ int64_t padded_ld(int64_t n) {
   return (n + 1) & ~int64_t(1);
 }
 
-// Largest Nm: a row of Nm complex128 entries spans at most 4 GiB.
-constexpr int64_t kMaxNm = int64_t(1) << 28;
+// Largest Nm: a row of Nm complex128 entries spans at most 2 GiB, so the
+// GEMV kernels' 32-bit in-row byte offsets and row buffer descriptors
+// cover it.
+constexpr int64_t kMaxNm = int64_t(1) << 27;
 
 bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
 
@@ -572,8 +574,7 @@ int fftmv_setup(fftmv_plan_t *out, const double *F_dev, int64_t Nm, int64_t Nd, 
   if (!out || !F_dev || !aligned8(F_dev) || Nm < 1 || Nd < 1 || Nt < 1) return FFTMV_ERR_INVALID_ARG;
   if (mask & ~(FFTMV_PREC_BITS | FFTMV_FLAG_BITS)) return FFTMV_ERR_INVALID_ARG;
   if (Nm > INT32_MAX || Nd > INT32_MAX) return FFTMV_ERR_UNSUPPORTED_SIZE;
-  // the GEMV kernels address a row of Fhat with 32-bit byte offsets: a
-  // complex128 row must stay within 4 GiB
+  // the GEMV kernels address a row of Fhat with 32-bit byte offsets
   if (Nm > kMaxNm) return FFTMV_ERR_UNSUPPORTED_SIZE;
   if (Nt > 4096) return FFTMV_ERR_UNSUPPORTED_SIZE;
   try {
@@ -641,7 +642,9 @@ const char *fftmv_status_string(int status) {
   switch (status) {
     case FFTMV_SUCCESS: return "success";
     case FFTMV_ERR_INVALID_ARG: return "invalid argument";
-    case FFTMV_ERR_UNSUPPORTED_SIZE: return "unsupported size (Nt above 4096, or above 2048 without a radix-2/3/5/7 factorisation)";
+    case FFTMV_ERR_UNSUPPORTED_SIZE:
+      return "unsupported size (Nm above 2^27, Nd above 2^31 - 1, Nt above 4096, or Nt above 2048 without a "
+             "radix-2/3/5/7 factorisation)";
     case FFTMV_ERR_OUT_OF_MEMORY: return "out of device memory";
     case FFTMV_ERR_HIP: return "HIP runtime error";
     case FFTMV_ERR_INTERNAL: return "internal error";

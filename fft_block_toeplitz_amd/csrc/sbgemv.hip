@@ -40,17 +40,24 @@ __device__ __forceinline__ void split(const f32x4 &f, cx<float> *o) {
 }
 __device__ __forceinline__ void split(const f64x2 &f, cx<double> *o) { o[0] = mk(f.x, f.y); }
 
-// Fhat is read once: non-temporal loads keep it from evicting the reused
-// per-frequency vectors from the caches.
-__device__ __forceinline__ f32x4 load_stream(const f32x4 *p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ f64x2 load_stream(const f64x2 *p) { return __builtin_nontemporal_load(p); }
-
-// base[off] with a wave-uniform base and a 32-bit byte offset: lets the
-// compiler use the scalar-base + 32-bit vector-offset form of the load and
-// keeps one VGPR per address instead of two.
+// A buffer descriptor over one row (raw: no stride, no swizzle; the fourth
+// word is the gfx9 value for untyped 32-bit data). A load through it is the
+// row base in scalar registers plus one 32-bit lane offset, so the per-lane
+// column offsets are the only address registers a lane keeps, and the
+// hardware returns zeros for an offset past the row's end instead of
+// reading beyond it.
+// The record count is the field's unsigned 32-bit pattern: rows of up to
+// 2^31 bytes (Nm <= 2^27 complex128 entries, checked at setup).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void *row, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(row), 0,
+                                           static_cast<int32_t>(static_cast<uint32_t>(bytes)), 0x00020000);
+}
+// 16 bytes at byte_off through a row descriptor, non-temporal (aux bit 1):
+// Fhat is read once, and streaming it past the caches keeps the reused
+// per-frequency vectors resident.
 template <typename V>
-__device__ __forceinline__ V load_stream_at(const V *base, uint32_t byte_off) {
-  return load_stream(reinterpret_cast<const V *>(reinterpret_cast<const char *>(base) + byte_off));
+__device__ __forceinline__ V load_stream_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_off), 0, 2));
 }
 
 // The Vec16<T>::n complex entries of the input vector that line up with
@@ -138,11 +145,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   const int64_t k = task / ngroups;
   const int64_t r0 = (task - k * ngroups) * R;
 
-  const V *rows[R];
+  // one buffer descriptor per row (scalar registers): a load is the row's
+  // descriptor plus the lane's 32-bit offset, shared by all R rows
+  __amdgpu_buffer_rsrc_t rows[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     int64_t r = r0 + i < Nd ? r0 + i : Nd - 1;  // tail group: re-read the last row, never store it
-    rows[i] = F + (k * Nd + r) * ldF_vec;
+    rows[i] = row_rsrc(F + (k * Nd + r) * ldF_vec, nvec * static_cast<int64_t>(sizeof(V)));
   }
   const cx<In> *xk = x + k * ldx;
 
@@ -160,7 +169,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < R; ++i)
-        fv[u][i] = load_stream_at(rows[i], static_cast<uint32_t>(j + u * kWave) * static_cast<uint32_t>(sizeof(V)));
+        fv[u][i] = load_stream_buf<V>(rows[i], static_cast<uint32_t>(j + u * kWave) * static_cast<uint32_t>(sizeof(V)));
 #pragma unroll
     for (int u = 0; u < U; ++u) load_x<T, In>(xk, j + u * kWave, xv[u]);
 #pragma unroll
@@ -179,7 +188,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE, WPE
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       cx<T> f[NV];
-      split(load_stream_at(rows[i], static_cast<uint32_t>(j) * static_cast<uint32_t>(sizeof(V))), f);
+      split(load_stream_buf<V>(rows[i], static_cast<uint32_t>(j) * static_cast<uint32_t>(sizeof(V))), f);
 #pragma unroll
       for (int e = 0; e < NV; ++e) fma_mul(ar[i][e % NC], ai[i][e % NC], f[e], xv[e]);
     }
@@ -208,11 +217,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE, WPE
 // time, keeping one partial sum per column: no cross-lane reduction. That
 // fits a lane in 64 VGPRs, so eight waves run per SIMD and every workgroup
 // of the Main shape (2 chunks x 1001 frequencies = 2002 workgroups on 2048
-// slots) is resident at once. Measured at Main: one row per load group at
-// eight waves per SIMD (600 us) beats two rows per group at four waves
-// (622 us), two partial sums per column at eight waves (641 us, spills) and
-// the rows split over two half-workgroups (630 us). d_k[r] is the same for
-// the whole workgroup (a scalar load, U rows per load).
+// slots) is resident at once. Each wave keeps ONE 16-byte load in flight
+// and waits for it before the next. Measured at Main: that (600 us, with
+// the loads through a row buffer descriptor; 604 us with 64-bit addresses,
+// which spill at 64 VGPRs) beats all VL loads of a row in flight (650 us),
+// two rows per load group at four waves per SIMD (622 us), two partial sums
+// per column (641 us, spills) and the rows split over two half-workgroups
+// (630 us). d_k[r] is the same for the whole workgroup (a scalar load, U
+// rows per load).
 template <typename T, typename In, int VL, int U>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void sbgemv_c_kernel(
     const typename Vec16<T>::type *__restrict__ F, const cx<In> *__restrict__ x, void *__restrict__ y, int64_t Nd,
@@ -238,28 +250,32 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
 #pragma unroll
     for (int e = 0; e < NV; ++e) ar[v][e] = ai[v][e] = T(0);
 
+  const int64_t row_bytes = nvec * static_cast<int64_t>(sizeof(V));
   int64_t r = 0;
   for (; r + U <= Nd; r += U) {
     cx<T> d[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) d[u] = cvt<T>(xk[r + u]);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(base + (r + u) * ldF_vec, row_bytes);
 #pragma unroll
       for (int v = 0; v < VL; ++v) {
         cx<T> f[NV];
-        split(load_stream_at(base + (r + u) * ldF_vec, off[v]), f);
+        split(load_stream_buf<V>(rs, off[v]), f);
 #pragma unroll
         for (int e = 0; e < NV; ++e) fma_conj_mul(ar[v][e], ai[v][e], f[e], d[u]);
-        __builtin_amdgcn_sched_barrier(0);  // one load group in flight per wave
+        __builtin_amdgcn_sched_barrier(0);  // one load in flight per wave
       }
+    }
   }
   for (; r < Nd; ++r) {  // fewer than U rows left
     const cx<T> d = cvt<T>(xk[r]);
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(base + r * ldF_vec, row_bytes);
 #pragma unroll
     for (int v = 0; v < VL; ++v) {
       cx<T> f[NV];
-      split(load_stream_at(base + r * ldF_vec, off[v]), f);
+      split(load_stream_buf<V>(rs, off[v]), f);
 #pragma unroll
       for (int e = 0; e < NV; ++e) fma_conj_mul(ar[v][e], ai[v][e], f[e], d);
     }

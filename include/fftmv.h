@@ -28,7 +28,7 @@
  *   d, v [Nt][Nd]
  * Pointers need 8-byte alignment (natural for double).
  *
- * Supported sizes: 1 <= Nm <= 2^28 (a complex128 row of Fhat within 4 GiB),
+ * Supported sizes: 1 <= Nm <= 2^27 (a complex128 row of Fhat within 2 GiB),
  * 1 <= Nd <= 2^31 - 1, and 1 <= Nt <= 4096 where
  *   - Nt = 2^a 3^b 5^c 7^d runs with radix 2/4/8, 3, 5 and 7 passes (except
  *     the few lengths above 3584 with a factor 7, whose radix-7 passes need

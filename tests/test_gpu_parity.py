@@ -280,7 +280,7 @@ def test_error_paths_on_device(fm):
     # an allocation that cannot succeed reports OUT_OF_MEMORY and leaks nothing
     free0 = torch.cuda.mem_get_info()[0]
     with pytest.raises(fm.FftmvError) as e:
-        fm.fftmv_setup(c.F_dev.data_ptr(), 1 << 30, 4096, 16, 0, 0)
+        fm.fftmv_setup(c.F_dev.data_ptr(), 1 << 27, 4096, 16, 0, 0)  # ~150 TB of Fhat
     assert e.value.status == fm.FFTMV_ERR_OUT_OF_MEMORY
     assert abs(torch.cuda.mem_get_info()[0] - free0) < (64 << 20)
 
