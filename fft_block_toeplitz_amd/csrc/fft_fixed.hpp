@@ -178,7 +178,13 @@ constexpr CtTile ct_wide_tile(int L) {
                    : CtTile{sizeof(T) == 4 ? 8 : 4, 1024};
 }
 constexpr bool has_ct(int L) { return L == 1000 || L == 2000; }
-constexpr int64_t kWideBatch = 4096;  // channels from which wide tiles pay
+// Channels from which the wide tile pays. Measured at Nt = 1000, forward
+// and inverse, FP32 and FP64: one channel per workgroup wins below ~256
+// channels (6.7 against 7.0 us) and collapses beyond ~1000, where its
+// 8-byte column reads fetch each cache line once per channel (FP32 forward,
+// 3072 channels: 120 us against 12.7; FP64, 2048: 96 against 29); from 512
+// channels the wide tile is ahead in all four kernels.
+constexpr int64_t kWideBatch = 512;
 
 }  // namespace
 }  // namespace fftmv

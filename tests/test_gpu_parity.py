@@ -88,7 +88,10 @@ SHAPES = [
     (1001, 3, 8),
     (2, 130, 40),    # Nd > Nm: tall blocks
     (129, 65, 1000), # Main's time length, ragged channel counts
-    (4103, 3, 1000), # wide batches (10-channel tiles, ragged last tile) at Main's length
+    (4103, 3, 1000), # wide batches (8-channel tiles, ragged last tile) at Main's length
+    (700, 3, 1000),  # the smallest wide batches (from 512 channels), ragged last tile
+    (3, 600, 1000),  # wide batches on the F* forward and F inverse side
+    (513, 2, 2000),  # wide batch at the Scale share's length, one channel in the last tile
     (33, 7, 2000),   # the Scale share's time length, narrow batches
     (3, 2, 4096),    # the longest supported transform, 2Nt = 2^13
     (2, 3, 3125),    # 2Nt = 2 * 5^5
