@@ -7,7 +7,7 @@
 namespace fftmv {
 
 constexpr int kWave = 64;
-constexpr int kBlock = 256;  // every kernel here runs 256-thread workgroups
+constexpr int kBlock = 256;  // the default workgroup size
 constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, one L2 each
 
 template <typename T>

@@ -36,10 +36,12 @@ namespace {
 // workgroup) so that every pass of the schedule fits. With C = 1 every
 // supported length (Nt <= 4096) fits.
 constexpr int kVmax = 20;
+// 1024-thread workgroups fit 128 VGPRs per lane: half the values per thread.
+constexpr int kVmaxWide = 10;
 // One Stockham pass of radix R over the [L][C] LDS tile. Butterfly j of
 // channel c reads elements j + q L/R, multiplies input q by
 // w_{Ns R}^{(j mod Ns) q} and writes output q to (j - j mod Ns) R + j mod Ns + q Ns.
-template <typename T, int R, int S, int VMAX>
+template <typename T, int R, int S, int VMAX, int TPB>
 __device__ __forceinline__ void lds_pass(cx<T> *lds, int L, int logC, int Ns, int twstep,
                                          const cx<T> *__restrict__ tw) {
   constexpr int B = VMAX / R;
@@ -49,7 +51,7 @@ __device__ __forceinline__ void lds_pass(cx<T> *lds, int L, int logC, int Ns, in
   cx<T> v[B][R];
 #pragma unroll
   for (int i = 0; i < B; ++i) {
-    int b = threadIdx.x + i * kBlock;
+    int b = threadIdx.x + i * TPB;
     if (b < nb) {
       int c = b & (C - 1), j = b >> logC;
 #pragma unroll
@@ -59,7 +61,7 @@ __device__ __forceinline__ void lds_pass(cx<T> *lds, int L, int logC, int Ns, in
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < B; ++i) {
-    int b = threadIdx.x + i * kBlock;
+    int b = threadIdx.x + i * TPB;
     if (b < nb) {
       int c = b & (C - 1), j = b >> logC;
       int k = j % Ns;
@@ -76,7 +78,7 @@ __device__ __forceinline__ void lds_pass(cx<T> *lds, int L, int logC, int Ns, in
 // First pass (Ns = 1, no twiddles): input n of this thread's channel comes
 // from get(n), output n goes to put(n, value). All loads of the thread are
 // issued before any butterfly.
-template <typename T, int R, int S, int VMAX, typename Get, typename Put>
+template <typename T, int R, int S, int VMAX, int TPB, typename Get, typename Put>
 __device__ __forceinline__ void first_pass(int L, int logC, Get get, Put put) {
   constexpr int B = VMAX / R;
   const int Lr = L / R;
@@ -84,7 +86,7 @@ __device__ __forceinline__ void first_pass(int L, int logC, Get get, Put put) {
   cx<T> v[B][R];
 #pragma unroll
   for (int i = 0; i < B; ++i) {
-    int b = threadIdx.x + i * kBlock;
+    int b = threadIdx.x + i * TPB;
     if (b < nb) {
       int j = b >> logC;
 #pragma unroll
@@ -93,7 +95,7 @@ __device__ __forceinline__ void first_pass(int L, int logC, Get get, Put put) {
   }
 #pragma unroll
   for (int i = 0; i < B; ++i) {
-    int b = threadIdx.x + i * kBlock;
+    int b = threadIdx.x + i * TPB;
     if (b < nb) {
       int j = b >> logC;
       dft<R, S>(v[i]);
@@ -104,7 +106,7 @@ __device__ __forceinline__ void first_pass(int L, int logC, Get get, Put put) {
 }
 
 // Last pass (Ns = L/R) reading the LDS tile and handing output n to put.
-template <typename T, int R, int S, int VMAX, typename Put>
+template <typename T, int R, int S, int VMAX, int TPB, typename Put>
 __device__ __forceinline__ void last_pass(const cx<T> *lds, int L, int logC, int twstep,
                                           const cx<T> *__restrict__ tw, Put put) {
   constexpr int B = VMAX / R;
@@ -114,7 +116,7 @@ __device__ __forceinline__ void last_pass(const cx<T> *lds, int L, int logC, int
   cx<T> v[B][R];
 #pragma unroll
   for (int i = 0; i < B; ++i) {
-    int b = threadIdx.x + i * kBlock;
+    int b = threadIdx.x + i * TPB;
     if (b < nb) {
       int c = b & (C - 1), j = b >> logC;
 #pragma unroll
@@ -123,7 +125,7 @@ __device__ __forceinline__ void last_pass(const cx<T> *lds, int L, int logC, int
   }
 #pragma unroll
   for (int i = 0; i < B; ++i) {
-    int b = threadIdx.x + i * kBlock;
+    int b = threadIdx.x + i * TPB;
     if (b < nb) {
       int j = b >> logC;
       if (Lr > 1) twiddle<T, R, S>(v[i], j, twstep, tw);
@@ -134,43 +136,43 @@ __device__ __forceinline__ void last_pass(const cx<T> *lds, int L, int logC, int
   }
 }
 
-template <typename T, int S, int VMAX>
+template <typename T, int S, int VMAX, int TPB>
 __device__ __forceinline__ void middle_passes(cx<T> *lds, const FftGeom &g, int first, int last, int logC,
                                               const cx<T> *__restrict__ tw) {
   for (int p = first; p < last; ++p) {
     switch (g.radix[p]) {
-      case 2: lds_pass<T, 2, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
-      case 3: lds_pass<T, 3, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
-      case 4: lds_pass<T, 4, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
-      case 5: lds_pass<T, 5, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
-      case 7: lds_pass<T, 7, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
-      default: lds_pass<T, 8, S, VMAX>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+      case 2: lds_pass<T, 2, S, VMAX, TPB>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+      case 3: lds_pass<T, 3, S, VMAX, TPB>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+      case 4: lds_pass<T, 4, S, VMAX, TPB>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+      case 5: lds_pass<T, 5, S, VMAX, TPB>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+      case 7: lds_pass<T, 7, S, VMAX, TPB>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
+      default: lds_pass<T, 8, S, VMAX, TPB>(lds, g.L, logC, g.ns[p], g.twstep[p], tw); break;
     }
   }
 }
 
-template <typename T, int S, int VMAX, typename Get, typename Put>
+template <typename T, int S, int VMAX, int TPB, typename Get, typename Put>
 __device__ __forceinline__ void first_pass_any(int R, int L, int logC, Get get, Put put) {
   switch (R) {
-    case 2: first_pass<T, 2, S, VMAX>(L, logC, get, put); break;
-    case 3: first_pass<T, 3, S, VMAX>(L, logC, get, put); break;
-    case 4: first_pass<T, 4, S, VMAX>(L, logC, get, put); break;
-    case 5: first_pass<T, 5, S, VMAX>(L, logC, get, put); break;
-    case 7: first_pass<T, 7, S, VMAX>(L, logC, get, put); break;
-    default: first_pass<T, 8, S, VMAX>(L, logC, get, put); break;
+    case 2: first_pass<T, 2, S, VMAX, TPB>(L, logC, get, put); break;
+    case 3: first_pass<T, 3, S, VMAX, TPB>(L, logC, get, put); break;
+    case 4: first_pass<T, 4, S, VMAX, TPB>(L, logC, get, put); break;
+    case 5: first_pass<T, 5, S, VMAX, TPB>(L, logC, get, put); break;
+    case 7: first_pass<T, 7, S, VMAX, TPB>(L, logC, get, put); break;
+    default: first_pass<T, 8, S, VMAX, TPB>(L, logC, get, put); break;
   }
 }
 
-template <typename T, int S, int VMAX, typename Put>
+template <typename T, int S, int VMAX, int TPB, typename Put>
 __device__ __forceinline__ void last_pass_any(int R, const cx<T> *lds, int L, int logC, int twstep,
                                               const cx<T> *__restrict__ tw, Put put) {
   switch (R) {
-    case 2: last_pass<T, 2, S, VMAX>(lds, L, logC, twstep, tw, put); break;
-    case 3: last_pass<T, 3, S, VMAX>(lds, L, logC, twstep, tw, put); break;
-    case 4: last_pass<T, 4, S, VMAX>(lds, L, logC, twstep, tw, put); break;
-    case 5: last_pass<T, 5, S, VMAX>(lds, L, logC, twstep, tw, put); break;
-    case 7: last_pass<T, 7, S, VMAX>(lds, L, logC, twstep, tw, put); break;
-    default: last_pass<T, 8, S, VMAX>(lds, L, logC, twstep, tw, put); break;
+    case 2: last_pass<T, 2, S, VMAX, TPB>(lds, L, logC, twstep, tw, put); break;
+    case 3: last_pass<T, 3, S, VMAX, TPB>(lds, L, logC, twstep, tw, put); break;
+    case 4: last_pass<T, 4, S, VMAX, TPB>(lds, L, logC, twstep, tw, put); break;
+    case 5: last_pass<T, 5, S, VMAX, TPB>(lds, L, logC, twstep, tw, put); break;
+    case 7: last_pass<T, 7, S, VMAX, TPB>(lds, L, logC, twstep, tw, put); break;
+    default: last_pass<T, 8, S, VMAX, TPB>(lds, L, logC, twstep, tw, put); break;
   }
 }
 template <typename T, typename Src, bool ROUND>
@@ -183,8 +185,8 @@ __device__ __forceinline__ T to_compute(Src v) {
 // BLUE: the length-L complex FFT in Bluestein form over an M-point tile
 // (g is then the schedule of M; tw stays the w_{2L} table, twM is w_{2M},
 // hM the filter's transform).
-template <typename T, typename Src, bool ROUND, int VMAX, bool OFF32, bool BLUE>
-__global__ __launch_bounds__(kBlock) void rfft_forward_kernel(FftGeom g, FwdFftArgs a, int logC,
+template <typename T, typename Src, bool ROUND, int VMAX, bool OFF32, bool BLUE, int TPB>
+__global__ __launch_bounds__(TPB) void rfft_forward_kernel(FftGeom g, FwdFftArgs a, int logC,
                                                               const cx<T> *__restrict__ tw, int64_t nblocks,
                                                               const cx<T> *__restrict__ twM,
                                                               const cx<T> *__restrict__ hM) {
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(kBlock) void rfft_forward_kernel(FftGeom g, FwdFftA
   const int L = static_cast<int>(a.Nt);
   // chirp c[m] = exp(-pi i m^2 / L) (m < L <= 2048: m^2 fits 32 bits)
   auto chirp = [&](int m) { return tw[(m * m) % (2 * L)]; };
-  const int c = threadIdx.x & (C - 1);  // fixed per thread: kBlock is a multiple of C
+  const int c = threadIdx.x & (C - 1);  // fixed per thread: TPB is a multiple of C
   const int64_t ch = xcd_contiguous_block(blockIdx.x, nblocks) * C + c;
   const bool live = ch < a.nchan;
   const Src *src = static_cast<const Src *>(a.src);
@@ -214,20 +216,20 @@ __global__ __launch_bounds__(kBlock) void rfft_forward_kernel(FftGeom g, FwdFftA
     // a[n] = z[n] c[n], zero up to M; a * conj(c) by M-point transforms
     const int M = g.L;
     auto get_a = [&](int n) { return n < L ? cmul(get(n), chirp(n)) : mk(T(0), T(0)); };
-    first_pass_any<T, -1, VMAX>(g.radix[0], M, logC, get_a, to_lds);
+    first_pass_any<T, -1, VMAX, TPB>(g.radix[0], M, logC, get_a, to_lds);
     __syncthreads();
-    middle_passes<T, -1, VMAX>(lds, g, 1, g.npass, logC, twM);
-    for (int i = threadIdx.x; i < (M << logC); i += kBlock) lds[i] = cmul(lds[i], hM[i >> logC]);
+    middle_passes<T, -1, VMAX, TPB>(lds, g, 1, g.npass, logC, twM);
+    for (int i = threadIdx.x; i < (M << logC); i += TPB) lds[i] = cmul(lds[i], hM[i >> logC]);
     __syncthreads();
-    middle_passes<T, +1, VMAX>(lds, g, 0, g.npass, logC, twM);
+    middle_passes<T, +1, VMAX, TPB>(lds, g, 0, g.npass, logC, twM);
   } else {
     if (g.npass == 0) {  // L == 1
       if (threadIdx.x < C) to_lds(0, get(0));
     } else {
-      first_pass_any<T, -1, VMAX>(g.radix[0], L, logC, get, to_lds);
+      first_pass_any<T, -1, VMAX, TPB>(g.radix[0], L, logC, get, to_lds);
     }
     __syncthreads();
-    middle_passes<T, -1, VMAX>(lds, g, 1, g.npass, logC, tw);
+    middle_passes<T, -1, VMAX, TPB>(lds, g, 1, g.npass, logC, tw);
   }
   // Z[k]: the tile entry (times c[k] in Bluestein form)
   auto zat = [&](int k, int ch) {
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kBlock) void rfft_forward_kernel(FftGeom g, FwdFftA
   // (frequency strides are even)
   const bool pack32 = two && d32b == d32a + 1 && (reinterpret_cast<uintptr_t>(d32a) & 15) == 0 &&
                       (a.fstride32 & 1) == 0;
-  for (int b = threadIdx.x; b < ((L + 1) << logh); b += kBlock) {
+  for (int b = threadIdx.x; b < ((L + 1) << logh); b += TPB) {
     const int k = b >> logh;
     const int ka = k == L ? 0 : k, kb = k == 0 ? 0 : L - k;
     const cx<T> w = tw[k];
@@ -288,8 +290,8 @@ __global__ __launch_bounds__(kBlock) void rfft_forward_kernel(FftGeom g, FwdFftA
 }
 
 // --------------------------------------------------------------- inverse
-template <typename T, typename Src, int VMAX, bool OFF32, bool BLUE>
-__global__ __launch_bounds__(kBlock) void rfft_inverse_kernel(FftGeom g, InvFftArgs a, int logC,
+template <typename T, typename Src, int VMAX, bool OFF32, bool BLUE, int TPB>
+__global__ __launch_bounds__(TPB) void rfft_inverse_kernel(FftGeom g, InvFftArgs a, int logC,
                                                               const cx<T> *__restrict__ tw, T inv_l,
                                                               int64_t nblocks, const cx<T> *__restrict__ twM,
                                                               const cx<T> *__restrict__ hM) {
@@ -351,14 +353,14 @@ __global__ __launch_bounds__(kBlock) void rfft_inverse_kernel(FftGeom g, InvFftA
     auto put_z = [&](int n, cx<T> v) {
       if (n < L) put(n, cmulc(v, chirp(n)));
     };
-    first_pass_any<T, -1, VMAX>(g.radix[0], M, logC, get_a, to_lds);
+    first_pass_any<T, -1, VMAX, TPB>(g.radix[0], M, logC, get_a, to_lds);
     __syncthreads();
-    middle_passes<T, -1, VMAX>(lds, g, 1, g.npass, logC, twM);
-    for (int i = threadIdx.x; i < (M << logC); i += kBlock) lds[i] = cmul(lds[i], hM[i >> logC]);
+    middle_passes<T, -1, VMAX, TPB>(lds, g, 1, g.npass, logC, twM);
+    for (int i = threadIdx.x; i < (M << logC); i += TPB) lds[i] = cmul(lds[i], hM[i >> logC]);
     __syncthreads();
-    middle_passes<T, +1, VMAX>(lds, g, 0, g.npass - 1, logC, twM);
+    middle_passes<T, +1, VMAX, TPB>(lds, g, 0, g.npass - 1, logC, twM);
     const int pl = g.npass - 1;
-    last_pass_any<T, +1, VMAX>(g.radix[pl], lds, M, logC, g.twstep[pl], twM, put_z);
+    last_pass_any<T, +1, VMAX, TPB>(g.radix[pl], lds, M, logC, g.twstep[pl], twM, put_z);
     return;
   }
   if (g.npass == 0) {  // L == 1
@@ -366,14 +368,14 @@ __global__ __launch_bounds__(kBlock) void rfft_inverse_kernel(FftGeom g, InvFftA
     return;
   }
   if (g.npass == 1) {
-    first_pass_any<T, +1, VMAX>(g.radix[0], L, logC, get, put);
+    first_pass_any<T, +1, VMAX, TPB>(g.radix[0], L, logC, get, put);
     return;
   }
-  first_pass_any<T, +1, VMAX>(g.radix[0], L, logC, get, to_lds);
+  first_pass_any<T, +1, VMAX, TPB>(g.radix[0], L, logC, get, to_lds);
   __syncthreads();
-  middle_passes<T, +1, VMAX>(lds, g, 1, g.npass - 1, logC, tw);
+  middle_passes<T, +1, VMAX, TPB>(lds, g, 1, g.npass - 1, logC, tw);
   const int pl = g.npass - 1;
-  last_pass_any<T, +1, VMAX>(g.radix[pl], lds, L, logC, g.twstep[pl], tw, put);
+  last_pass_any<T, +1, VMAX, TPB>(g.radix[pl], lds, L, logC, g.twstep[pl], tw, put);
 }
 
 int ilog2(int c) {
@@ -385,25 +387,56 @@ int ilog2(int c) {
 // Launch one batched transform with the generic kernels. tile: the
 // schedule of the LDS tile (length L, or M in Bluestein form); twM, hM: the
 // Bluestein tables (BLUE only).
+// Wide workgroups may take more than 64 KiB of dynamic LDS: raise the
+// kernel's limit once (the caller keeps one static per kernel).
+inline hipError_t allow_wide_lds(const void *kernel) {
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsWide);
+}
+
+template <typename T, typename Src, bool ROUND, bool BLUE, int TPB>
+void fwd_tpb(const FftGeom &tile, const FwdFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
+             const void *hM, hipStream_t s) {
+  const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
+  const size_t lds = static_cast<size_t>(tile.L) * cfg.C * sizeof(cx<T>);
+  auto *k = &rfft_forward_kernel<T, Src, ROUND, TPB == kBlockWide ? kVmaxWide : kVmax, false, BLUE, TPB>;
+  if constexpr (TPB == kBlockWide) {
+    static const hipError_t raised = allow_wide_lds(reinterpret_cast<const void *>(k));
+    (void)raised;
+  }
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(nblocks)), dim3(TPB), lds, s, tile, a, ilog2(cfg.C),
+                     static_cast<const cx<T> *>(tw), nblocks, static_cast<const cx<T> *>(twM),
+                     static_cast<const cx<T> *>(hM));
+}
 template <typename T, typename Src, bool ROUND, bool BLUE>
 void fwd(const FftGeom &tile, const FwdFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
          const void *hM, hipStream_t s) {
-  const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
-  const size_t lds = static_cast<size_t>(tile.L) * cfg.C * sizeof(cx<T>);
-  hipLaunchKernelGGL((rfft_forward_kernel<T, Src, ROUND, kVmax, false, BLUE>), dim3(static_cast<unsigned>(nblocks)),
-                     dim3(kBlock), lds, s, tile, a, ilog2(cfg.C), static_cast<const cx<T> *>(tw), nblocks,
-                     static_cast<const cx<T> *>(twM), static_cast<const cx<T> *>(hM));
+  if (cfg.tpb == kBlockWide)
+    fwd_tpb<T, Src, ROUND, BLUE, kBlockWide>(tile, a, cfg, tw, twM, hM, s);
+  else
+    fwd_tpb<T, Src, ROUND, BLUE, kBlock>(tile, a, cfg, tw, twM, hM, s);
 }
 
+template <typename T, typename Src, bool BLUE, int TPB>
+void inv_tpb(const FftGeom &tile, const InvFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
+             const void *hM, hipStream_t s) {
+  const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
+  const size_t lds = static_cast<size_t>(tile.L) * cfg.C * sizeof(cx<T>);
+  auto *k = &rfft_inverse_kernel<T, Src, TPB == kBlockWide ? kVmaxWide : kVmax, false, BLUE, TPB>;
+  if constexpr (TPB == kBlockWide) {
+    static const hipError_t raised = allow_wide_lds(reinterpret_cast<const void *>(k));
+    (void)raised;
+  }
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(nblocks)), dim3(TPB), lds, s, tile, a, ilog2(cfg.C),
+                     static_cast<const cx<T> *>(tw), T(1) / static_cast<T>(a.Nt), nblocks,
+                     static_cast<const cx<T> *>(twM), static_cast<const cx<T> *>(hM));
+}
 template <typename T, typename Src, bool BLUE>
 void inv(const FftGeom &tile, const InvFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
          const void *hM, hipStream_t s) {
-  const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
-  const size_t lds = static_cast<size_t>(tile.L) * cfg.C * sizeof(cx<T>);
-  hipLaunchKernelGGL((rfft_inverse_kernel<T, Src, kVmax, false, BLUE>), dim3(static_cast<unsigned>(nblocks)),
-                     dim3(kBlock), lds, s, tile, a, ilog2(cfg.C), static_cast<const cx<T> *>(tw),
-                     T(1) / static_cast<T>(a.Nt), nblocks, static_cast<const cx<T> *>(twM),
-                     static_cast<const cx<T> *>(hM));
+  if (cfg.tpb == kBlockWide)
+    inv_tpb<T, Src, BLUE, kBlockWide>(tile, a, cfg, tw, twM, hM, s);
+  else
+    inv_tpb<T, Src, BLUE, kBlock>(tile, a, cfg, tw, twM, hM, s);
 }
 
 // the element types of one launch

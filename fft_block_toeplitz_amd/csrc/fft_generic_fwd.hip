@@ -9,21 +9,40 @@ namespace fftmv {
 // Channels per workgroup for a schedule, precision and batch: the widest C
 // that still gives at least 1024 workgroups (four per CU); for small batches
 // the narrowest C (most workgroups). C = 0 when the transform does not fit.
+// Channels per workgroup: the widest tile that still leaves at least
+// kMinFftBlocks workgroups (one per CU), else the narrowest tile that fits
+// (small batches). Wide tiles read and write each time step and frequency
+// in runs of C channels, where one channel per workgroup reads every cache
+// line once per channel. The workgroup has 1024 threads (half the registers
+// per thread, more LDS) when 256 threads cannot hold a pass's butterflies,
+// or when there are fewer than two workgroups per CU: a 256-thread
+// workgroup then leaves each CU with 4 to 8 waves to hide memory latency.
+// Measured at Nt = 256, 1009 (Bluestein), 1024 and 1029, 128 to 8192
+// channels, FP32 and FP64.
+constexpr int64_t kMinFftBlocks = 256;
+
 FftLaunch fft_launch_config(const FftGeom &g, bool f32, int64_t nchan) {
   const int64_t esz = f32 ? 8 : 16;
-  auto fits = [&](int C) {
-    if (static_cast<int64_t>(g.L) * C * esz > kMaxLds) return false;
+  auto fits = [&](int C, int tpb) {
+    const int64_t lds_cap = tpb == kBlockWide ? kMaxLdsWide : kMaxLds;
+    const int vmax = tpb == kBlockWide ? kVmaxWide : kVmax;
+    if (static_cast<int64_t>(g.L) * C * esz > lds_cap) return false;
     for (int p = 0; p < g.npass; ++p) {
       const int64_t nb = static_cast<int64_t>(g.L / g.radix[p]) * C;
-      if (nb > static_cast<int64_t>(kVmax / g.radix[p]) * kBlock) return false;
+      if (nb > static_cast<int64_t>(vmax / g.radix[p]) * tpb) return false;
     }
     return true;
   };
+  auto cfg = [](int C, bool wide) {
+    return FftLaunch{C, wide ? kVmaxWide : kVmax, wide ? kBlockWide : kBlock};
+  };
   FftLaunch narrowest;
   for (int C = kMaxChannelsPerBlock; C >= 1; C >>= 1) {
-    if (!fits(C)) continue;
-    if ((nchan + C - 1) / C >= 1024) return {C, kVmax};
-    narrowest = {C, kVmax};
+    const bool f256 = fits(C, kBlock), f1024 = fits(C, kBlockWide);
+    if (!f256 && !f1024) continue;
+    const int64_t nblocks = (nchan + C - 1) / C;
+    if (nblocks >= kMinFftBlocks) return cfg(C, f1024 && (!f256 || nblocks < 2 * kMinFftBlocks));
+    narrowest = cfg(C, !f256);
   }
   return narrowest;
 }

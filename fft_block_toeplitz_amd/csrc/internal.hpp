@@ -7,7 +7,9 @@
 namespace fftmv {
 
 constexpr int kMaxPasses = 24;
-constexpr int kMaxLds = 65536;  // bytes of LDS one FFT workgroup may use
+constexpr int kMaxLds = 65536;      // bytes of LDS a 256-thread FFT workgroup may use
+constexpr int kBlockWide = 1024;    // threads of a wide FFT workgroup
+constexpr int kMaxLdsWide = 81920;  // LDS of a wide FFT workgroup: two fit a CU's 160 KiB
 constexpr int kMaxChannelsPerBlock = 32;
 
 // Stockham radix schedule of the length-L complex FFT that carries the
@@ -132,11 +134,13 @@ struct CastArgs {
   bool dst_f32 = false;
 };
 
-// FFT launch shape: C channels per workgroup (power of two) and the
-// per-thread register budget VMAX (complex values held during a pass).
+// FFT launch shape: C channels per workgroup (power of two), the
+// per-thread register budget VMAX (complex values held during a pass) and
+// the workgroup size (kBlock or kBlockWide threads).
 struct FftLaunch {
   int C = 0;
   int vmax = 0;
+  int tpb = 0;
 };
 FftLaunch fft_launch_config(const FftGeom &g, bool f32, int64_t nchan);
 // Channels per FFT workgroup for this schedule, precision and batch size; 0

@@ -30,9 +30,7 @@
  *
  * Supported sizes: 1 <= Nm <= 2^27 (a complex128 row of Fhat within 2 GiB),
  * 1 <= Nd <= 2^31 - 1, and 1 <= Nt <= 4096 where
- *   - Nt = 2^a 3^b 5^c 7^d runs with radix 2/4/8, 3, 5 and 7 passes (except
- *     the few lengths above 3584 with a factor 7, whose radix-7 passes need
- *     more registers than a workgroup holds), and
+ *   - Nt = 2^a 3^b 5^c 7^d runs with radix 2/4/8, 3, 5 and 7 passes, and
  *   - any other Nt <= 2048 runs in Bluestein (chirp-z) form: the length-Nt
  *     transform as a circular convolution of a power-of-two length
  *     M >= 2 Nt - 1;

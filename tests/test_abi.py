@@ -63,7 +63,7 @@ FAKE = 0x10000  # never dereferenced: every case below fails validation first
     ((FAKE, 8, 4, 2053, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE),     # prime above 2048: no radix schedule,
                                                                 # Bluestein tile too large
     ((FAKE, 8, 4, 2 * 2053, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE), # the same factor
-    ((FAKE, 8, 4, 3920, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE),     # 2^4 5 7^2: radix-7 passes do not fit
+    ((FAKE, 8, 4, 4093, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE),     # prime above 2048
     ((FAKE, 8, 4, 5000, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE),     # Nt > 4096
     ((FAKE, 1 << 31, 4, 16, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE), # Nm too large
     ((FAKE, (1 << 27) + 1, 4, 16, 0), fm.FFTMV_ERR_UNSUPPORTED_SIZE),  # complex128 row above 2 GiB

@@ -103,14 +103,19 @@ SHAPES = [
     (11, 3, 360),    # 2^3 3^2 5
     (7, 3, 1029),    # 3 * 7^3
     (3, 2, 2187),    # 3^7
-    (2, 2, 3584),    # 2^9 7: the longest radix-7 length that fits
-    (129, 33, 105),  # 3 5 7, wide batch (many channels per workgroup)
+    (2, 2, 3584),    # 2^9 7
+    (2, 2, 3920),    # 2^4 5 7^2: radix-7 passes in a 1024-thread workgroup
+    (3, 2, 3969),    # 3^4 7^2
+    (129, 33, 105),  # 3 5 7; its frequency blocks (4257 channels) take 16-channel, 1024-thread tiles
+    (2048, 2, 1029), # 1024-thread tiles in the applies: radix-7 passes need them, FP64 tiles of 66 KB LDS
     # Bluestein form (lengths with other prime factors)
     (5, 3, 11),      # M = 32
     (4, 2, 13),
     (3, 3, 97),
     (129, 33, 101),  # wide batch, M = 256
     (6, 4, 1009),
+    (600, 2, 1009),  # Bluestein in 1024-thread tiles (fewer than two workgroups per CU)
+    (1024, 2, 1009), # Bluestein FP32 tiles of 4 channels, which only 1024 threads hold
     (7, 5, 1001),    # 7 11 13
     (2, 2, 2039),    # the longest prime in Bluestein form, M = 4096
 ]

@@ -162,10 +162,25 @@ def test_invalid_arguments(args):
         fm.fftmv_predict(10, 4, 8, 0, 0, 0, 1.0, [1.0] * 8)
 
 
-@pytest.mark.parametrize("Nt", [2053, 4093, 3920, 4097])
+@pytest.mark.parametrize("Nt", [2053, 3001, 4093, 4097])
 def test_unsupported_lengths(Nt):
     with pytest.raises(fm.FftmvError) as e:
         fm.fftmv_predict(10, 4, Nt, 0, 0, 0, 1.0)
     assert e.value.status == fm.FFTMV_ERR_UNSUPPORTED_SIZE
     with pytest.raises(fm.FftmvError):
         fm.fftmv_select_precision(10, 4, Nt, 0, 0, 1.0, 1e-6)
+
+
+def test_every_smooth_length_up_to_4096_is_supported():
+    """Nt = 2^a 3^b 5^c 7^d <= 4096 has a radix schedule that fits a
+    workgroup (the longest radix-7 ones in 1024-thread workgroups), and a
+    prime up to 2048 has a Bluestein tile."""
+    def smooth(n):
+        for p in (2, 3, 5, 7):
+            while n % p == 0:
+                n //= p
+        return n == 1
+
+    lengths = [n for n in range(1, 4097) if smooth(n)] + [2039, 2027, 1009, 11]
+    for Nt in lengths:
+        fm.fftmv_predict(10, 4, Nt, 0, 0, 0, 1.0)  # raises if unsupported
