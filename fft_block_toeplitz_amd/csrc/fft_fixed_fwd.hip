@@ -115,7 +115,13 @@ void launch_fwd_ct(const FwdFftArgs &a, const void *tw, hipStream_t s) {
 
 template <typename T, int L, bool ROUND, typename Src = double>
 void launch_fwd_ct_c(const FwdFftArgs &a, const void *tw, hipStream_t s) {
-  constexpr CtTile w = ct_wide_tile<T>(L);
+  constexpr CtTile w = ct_wide_tile<T>(L), x = ct_wider_fwd_tile<T>(L);
+  if constexpr (x.C != w.C || x.tpb != w.tpb) {
+    if (a.nchan >= kWiderBatch) {
+      launch_fwd_ct<T, L, ROUND, Src, x.C, x.tpb>(a, tw, s);
+      return;
+    }
+  }
   if (a.nchan >= kWideBatch)
     launch_fwd_ct<T, L, ROUND, Src, w.C, w.tpb>(a, tw, s);
   else
