@@ -31,12 +31,13 @@
 namespace fftmv {
 namespace {
 
-// A thread keeps at most kVmax complex values in registers during a pass,
-// i.e. kVmax / R butterflies of radix R; the host picks C (channels per
-// workgroup) so that every pass of the schedule fits. With C = 1 every
-// supported length (Nt <= 4096) fits.
+// A thread keeps at most VMAX complex values in registers during a pass,
+// i.e. VMAX / R butterflies of radix R: kVmax in 256-thread workgroups,
+// kVmaxWide in 1024-thread ones (which fit 128 VGPRs per lane). The host
+// picks C (channels per workgroup) and the workgroup size so that every
+// pass of the schedule fits; with C = 1 every supported length fits, the
+// longest radix-7 schedules (Nt above 3584) in 1024-thread workgroups.
 constexpr int kVmax = 20;
-// 1024-thread workgroups fit 128 VGPRs per lane: half the values per thread.
 constexpr int kVmaxWide = 10;
 // One Stockham pass of radix R over the [L][C] LDS tile. Butterfly j of
 // channel c reads elements j + q L/R, multiplies input q by
