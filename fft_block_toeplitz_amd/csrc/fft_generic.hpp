@@ -26,6 +26,9 @@
 // tiles, which share cache lines, share an L2.
 #pragma once
 
+#include <atomic>
+#include <cstdint>
+
 #include "fft_device.hpp"
 
 namespace fftmv {
@@ -389,103 +392,100 @@ int ilog2(int c) {
 // schedule of the LDS tile (length L, or M in Bluestein form); twM, hM: the
 // Bluestein tables (BLUE only).
 // Wide workgroups may take more than 64 KiB of dynamic LDS: raise the
-// kernel's limit once (the caller keeps one static per kernel).
-inline hipError_t allow_wide_lds(const void *kernel) {
-  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsWide);
+// kernel's limit, once per device (a function attribute is per device);
+// `done` holds one bit per device already raised.
+inline hipError_t raise_wide_lds(const void *kernel, std::atomic<uint64_t> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsWide);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
 }
 
 template <typename T, typename Src, bool ROUND, bool BLUE, int TPB>
-void fwd_tpb(const FftGeom &tile, const FwdFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
-             const void *hM, hipStream_t s) {
+hipError_t fwd_tpb(const FftGeom &tile, const FwdFftArgs &a, const FftLaunch &cfg, const void *tw,
+                   const void *twM, const void *hM, hipStream_t s) {
   const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
   const size_t lds = static_cast<size_t>(tile.L) * cfg.C * sizeof(cx<T>);
   auto *k = &rfft_forward_kernel<T, Src, ROUND, TPB == kBlockWide ? kVmaxWide : kVmax, false, BLUE, TPB>;
   if constexpr (TPB == kBlockWide) {
-    static const hipError_t raised = allow_wide_lds(reinterpret_cast<const void *>(k));
-    (void)raised;
+    static std::atomic<uint64_t> raised{0};
+    const hipError_t e = raise_wide_lds(reinterpret_cast<const void *>(k), raised);
+    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(nblocks)), dim3(TPB), lds, s, tile, a, ilog2(cfg.C),
                      static_cast<const cx<T> *>(tw), nblocks, static_cast<const cx<T> *>(twM),
                      static_cast<const cx<T> *>(hM));
+  return hipSuccess;
 }
 template <typename T, typename Src, bool ROUND, bool BLUE>
-void fwd(const FftGeom &tile, const FwdFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
-         const void *hM, hipStream_t s) {
-  if (cfg.tpb == kBlockWide)
-    fwd_tpb<T, Src, ROUND, BLUE, kBlockWide>(tile, a, cfg, tw, twM, hM, s);
-  else
-    fwd_tpb<T, Src, ROUND, BLUE, kBlock>(tile, a, cfg, tw, twM, hM, s);
+hipError_t fwd(const FftGeom &tile, const FwdFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
+               const void *hM, hipStream_t s) {
+  if (cfg.tpb == kBlockWide) return fwd_tpb<T, Src, ROUND, BLUE, kBlockWide>(tile, a, cfg, tw, twM, hM, s);
+  return fwd_tpb<T, Src, ROUND, BLUE, kBlock>(tile, a, cfg, tw, twM, hM, s);
 }
 
 template <typename T, typename Src, bool BLUE, int TPB>
-void inv_tpb(const FftGeom &tile, const InvFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
-             const void *hM, hipStream_t s) {
+hipError_t inv_tpb(const FftGeom &tile, const InvFftArgs &a, const FftLaunch &cfg, const void *tw,
+                   const void *twM, const void *hM, hipStream_t s) {
   const int64_t nblocks = (a.nchan + cfg.C - 1) / cfg.C;
   const size_t lds = static_cast<size_t>(tile.L) * cfg.C * sizeof(cx<T>);
   auto *k = &rfft_inverse_kernel<T, Src, TPB == kBlockWide ? kVmaxWide : kVmax, false, BLUE, TPB>;
   if constexpr (TPB == kBlockWide) {
-    static const hipError_t raised = allow_wide_lds(reinterpret_cast<const void *>(k));
-    (void)raised;
+    static std::atomic<uint64_t> raised{0};
+    const hipError_t e = raise_wide_lds(reinterpret_cast<const void *>(k), raised);
+    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(nblocks)), dim3(TPB), lds, s, tile, a, ilog2(cfg.C),
                      static_cast<const cx<T> *>(tw), T(1) / static_cast<T>(a.Nt), nblocks,
                      static_cast<const cx<T> *>(twM), static_cast<const cx<T> *>(hM));
+  return hipSuccess;
 }
 template <typename T, typename Src, bool BLUE>
-void inv(const FftGeom &tile, const InvFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
-         const void *hM, hipStream_t s) {
-  if (cfg.tpb == kBlockWide)
-    inv_tpb<T, Src, BLUE, kBlockWide>(tile, a, cfg, tw, twM, hM, s);
-  else
-    inv_tpb<T, Src, BLUE, kBlock>(tile, a, cfg, tw, twM, hM, s);
+hipError_t inv(const FftGeom &tile, const InvFftArgs &a, const FftLaunch &cfg, const void *tw, const void *twM,
+               const void *hM, hipStream_t s) {
+  if (cfg.tpb == kBlockWide) return inv_tpb<T, Src, BLUE, kBlockWide>(tile, a, cfg, tw, twM, hM, s);
+  return inv_tpb<T, Src, BLUE, kBlock>(tile, a, cfg, tw, twM, hM, s);
 }
 
 // the element types of one launch
 template <bool BLUE>
-void fwd_any(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg, const void *tw,
-             const void *twM, const void *hM, hipStream_t s) {
+hipError_t fwd_any(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+                   const void *tw, const void *twM, const void *hM, hipStream_t s) {
   if (compute_f32) {
-    if (a.src_f32)
-      fwd<float, float, false, BLUE>(tile, a, cfg, tw, twM, hM, s);
-    else
-      fwd<float, double, false, BLUE>(tile, a, cfg, tw, twM, hM, s);
-  } else {
-    if (a.src_f32)
-      fwd<double, float, false, BLUE>(tile, a, cfg, tw, twM, hM, s);
-    else if (a.round_f32)
-      fwd<double, double, true, BLUE>(tile, a, cfg, tw, twM, hM, s);
-    else
-      fwd<double, double, false, BLUE>(tile, a, cfg, tw, twM, hM, s);
+    if (a.src_f32) return fwd<float, float, false, BLUE>(tile, a, cfg, tw, twM, hM, s);
+    return fwd<float, double, false, BLUE>(tile, a, cfg, tw, twM, hM, s);
   }
+  if (a.src_f32) return fwd<double, float, false, BLUE>(tile, a, cfg, tw, twM, hM, s);
+  if (a.round_f32) return fwd<double, double, true, BLUE>(tile, a, cfg, tw, twM, hM, s);
+  return fwd<double, double, false, BLUE>(tile, a, cfg, tw, twM, hM, s);
 }
 
 template <bool BLUE>
-void inv_any(const FftGeom &tile, const InvFftArgs &a, bool compute_f32, const FftLaunch &cfg, const void *tw,
-             const void *twM, const void *hM, hipStream_t s) {
+hipError_t inv_any(const FftGeom &tile, const InvFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+                   const void *tw, const void *twM, const void *hM, hipStream_t s) {
   if (compute_f32) {
-    if (a.src_f32)
-      inv<float, float, BLUE>(tile, a, cfg, tw, twM, hM, s);
-    else
-      inv<float, double, BLUE>(tile, a, cfg, tw, twM, hM, s);
-  } else {
-    if (a.src_f32)
-      inv<double, float, BLUE>(tile, a, cfg, tw, twM, hM, s);
-    else
-      inv<double, double, BLUE>(tile, a, cfg, tw, twM, hM, s);
+    if (a.src_f32) return inv<float, float, BLUE>(tile, a, cfg, tw, twM, hM, s);
+    return inv<float, double, BLUE>(tile, a, cfg, tw, twM, hM, s);
   }
+  if (a.src_f32) return inv<double, float, BLUE>(tile, a, cfg, tw, twM, hM, s);
+  return inv<double, double, BLUE>(tile, a, cfg, tw, twM, hM, s);
 }
 
 }  // namespace
 
 // Generic launches, one translation unit each (fft_generic_*.hip) so that
 // they compile in parallel; the Bluestein ones take the M-point tables.
-void generic_forward(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+hipError_t generic_forward(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg,
                      const void *tw, hipStream_t s);
-void generic_forward_blue(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+hipError_t generic_forward_blue(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg,
                           const void *tw, const void *twM, const void *hM, hipStream_t s);
-void generic_inverse(const FftGeom &tile, const InvFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+hipError_t generic_inverse(const FftGeom &tile, const InvFftArgs &a, bool compute_f32, const FftLaunch &cfg,
                      const void *tw, hipStream_t s);
-void generic_inverse_blue(const FftGeom &tile, const InvFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+hipError_t generic_inverse_blue(const FftGeom &tile, const InvFftArgs &a, bool compute_f32, const FftLaunch &cfg,
                           const void *tw, const void *twM, const void *hM, hipStream_t s);
 
 }  // namespace fftmv

@@ -58,9 +58,9 @@ int64_t bluestein_length(int64_t L) {
   return M;
 }
 
-void generic_forward(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+hipError_t generic_forward(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg,
                      const void *tw, hipStream_t s) {
-  fwd_any<false>(tile, a, compute_f32, cfg, tw, nullptr, nullptr, s);
+  return fwd_any<false>(tile, a, compute_f32, cfg, tw, nullptr, nullptr, s);
 }
 
 hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
@@ -72,9 +72,11 @@ hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool comput
   if (blue) {
     const void *twM = compute_f32 ? blue->tw32 : blue->tw64, *hM = compute_f32 ? blue->hf32 : blue->hf64;
     if (!twM || !hM) return hipErrorInvalidValue;
-    generic_forward_blue(tile, a, compute_f32, cfg, tw, twM, hM, s);
+    const hipError_t e = generic_forward_blue(tile, a, compute_f32, cfg, tw, twM, hM, s);
+    if (e != hipSuccess) return e;
   } else {
-    generic_forward(tile, a, compute_f32, cfg, tw, s);
+    const hipError_t e = generic_forward(tile, a, compute_f32, cfg, tw, s);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }

@@ -4,9 +4,9 @@
 
 namespace fftmv {
 
-void generic_forward_blue(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+hipError_t generic_forward_blue(const FftGeom &tile, const FwdFftArgs &a, bool compute_f32, const FftLaunch &cfg,
                           const void *tw, const void *twM, const void *hM, hipStream_t s) {
-  fwd_any<true>(tile, a, compute_f32, cfg, tw, twM, hM, s);
+  return fwd_any<true>(tile, a, compute_f32, cfg, tw, twM, hM, s);
 }
 
 }  // namespace fftmv

@@ -6,9 +6,9 @@
 
 namespace fftmv {
 
-void generic_inverse(const FftGeom &tile, const InvFftArgs &a, bool compute_f32, const FftLaunch &cfg,
+hipError_t generic_inverse(const FftGeom &tile, const InvFftArgs &a, bool compute_f32, const FftLaunch &cfg,
                      const void *tw, hipStream_t s) {
-  inv_any<false>(tile, a, compute_f32, cfg, tw, nullptr, nullptr, s);
+  return inv_any<false>(tile, a, compute_f32, cfg, tw, nullptr, nullptr, s);
 }
 
 hipError_t launch_fft_inverse(const FftGeom &g, const InvFftArgs &a, bool compute_f32, const void *tw,
@@ -20,9 +20,11 @@ hipError_t launch_fft_inverse(const FftGeom &g, const InvFftArgs &a, bool comput
   if (blue) {
     const void *twM = compute_f32 ? blue->tw32 : blue->tw64, *hM = compute_f32 ? blue->hi32 : blue->hi64;
     if (!twM || !hM) return hipErrorInvalidValue;
-    generic_inverse_blue(tile, a, compute_f32, cfg, tw, twM, hM, s);
+    const hipError_t e = generic_inverse_blue(tile, a, compute_f32, cfg, tw, twM, hM, s);
+    if (e != hipSuccess) return e;
   } else {
-    generic_inverse(tile, a, compute_f32, cfg, tw, s);
+    const hipError_t e = generic_inverse(tile, a, compute_f32, cfg, tw, s);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }
