@@ -12,6 +12,8 @@
 // FP32 sums use many short chains (lanes x unrolled slots) and a tree at the
 // end, never one long serial chain: with n = 5000 a single FP32 chain alone
 // would cost ~1e-6 relative error.
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -310,19 +312,68 @@ void launch_c(const SbgemvArgs &a, int64_t nvec, int64_t nchunks, hipStream_t s)
                      a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks);
 }
 
+// Workgroups of the conjugate-transpose kernel that one CU holds at once:
+// 64 VGPRs and no LDS give eight waves on each of four SIMDs, four waves per
+// workgroup.
+constexpr int kResidentPerCuC = 8;
+// A narrower column chunk is taken only when it fills the rounds of
+// resident workgroups better than the current pick by more than this.
+constexpr double kFillMargin = 0.05;
+
+int resident_c_workgroups() {
+  static std::atomic<int> cus_of[64];  // per device, 0 until queried
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev >= 0 && dev < 64) cus = cus_of[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev >= 0 && dev < 64) cus_of[dev].store(cus, std::memory_order_relaxed);
+  }
+  return kResidentPerCuC * cus;
+}
+
+struct ChunksC {
+  int64_t vl = 1, nchunks = 1;
+};
+
+// Column chunks of one frequency for the conjugate-transpose kernel. A
+// workgroup holds its chunk for all Nd rows with one load in flight per
+// wave, so a launch that overflows the resident workgroups by a few leaves
+// those few to run almost alone at the end: at Nm = 5000, Nt = 1029 (1030
+// frequencies) two chunks per frequency make 2060 workgroups on 2048 slots
+// and take 808 us, five chunks (2 vectors per lane, 5150 workgroups, the
+// last round 51% full) 669 us. For each width of 5 down to 1 vectors per
+// lane (then the fewest, equal chunks that cover the row) this takes the
+// fill of the rounds, workgroups / (rounds x slots), and keeps the widest
+// chunk unless a narrower one fills clearly better: the Main and Scale
+// shapes keep 5 vectors per lane (fill 0.978 and 0.977).
+ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots) {
+  ChunksC best;
+  double best_fill = -1.0;
+  for (int64_t m = kMaxVecsC; m >= 1; --m) {
+    const int64_t nch0 = (nvec + kBlock * m - 1) / (kBlock * m);
+    const int64_t vl = (nvec + nch0 * kBlock - 1) / (nch0 * kBlock);
+    const int64_t nch = (nvec + vl * kBlock - 1) / (vl * kBlock);
+    const int64_t n = K * nch;
+    const int64_t rounds = (n + slots - 1) / slots;
+    const double fill = static_cast<double>(n) / static_cast<double>(rounds * slots);
+    if (fill > best_fill + kFillMargin) {
+      best = {vl, nch};
+      best_fill = fill;
+    }
+  }
+  return best;
+}
+
 template <typename T, typename In>
 void launch_c_vl(const SbgemvArgs &a, int64_t nvec, hipStream_t s) {
-  // fewest chunks of at most kMaxVecsC*256 vectors, then the smallest VL
-  // that still covers the row: chunks of (nearly) equal length
-  const int64_t nchunks = (nvec + kBlock * kMaxVecsC - 1) / (kBlock * kMaxVecsC);
-  const int64_t vl = (nvec + nchunks * kBlock - 1) / (nchunks * kBlock);
-  const int64_t nch = (nvec + vl * kBlock - 1) / (vl * kBlock);
-  switch (vl) {
-    case 1: launch_c<T, In, 1>(a, nvec, nch, s); break;
-    case 2: launch_c<T, In, 2>(a, nvec, nch, s); break;
-    case 3: launch_c<T, In, 3>(a, nvec, nch, s); break;
-    case 4: launch_c<T, In, 4>(a, nvec, nch, s); break;
-    default: launch_c<T, In, 5>(a, nvec, nch, s); break;
+  const ChunksC c = choose_chunks_c(a.K, nvec, resident_c_workgroups());
+  switch (c.vl) {
+    case 1: launch_c<T, In, 1>(a, nvec, c.nchunks, s); break;
+    case 2: launch_c<T, In, 2>(a, nvec, c.nchunks, s); break;
+    case 3: launch_c<T, In, 3>(a, nvec, c.nchunks, s); break;
+    case 4: launch_c<T, In, 4>(a, nvec, c.nchunks, s); break;
+    default: launch_c<T, In, 5>(a, nvec, c.nchunks, s); break;
   }
 }
 
