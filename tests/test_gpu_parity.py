@@ -86,6 +86,8 @@ SHAPES = [
     (1, 1, 1),       # 2Nt = 2
     (1, 1, 5),       # odd Nt
     (1001, 3, 8),
+    (1400, 3, 16),   # conjugate-transpose GEMV: 3 column vectors per lane in FP32
+    (1800, 3, 16),   # ... and 4
     (2, 130, 40),    # Nd > Nm: tall blocks
     (129, 65, 1000), # Main's time length, ragged channel counts
     (4103, 3, 1000), # wide batches (8-channel tiles, ragged last tile) at Main's length
