@@ -295,9 +295,24 @@ hipError_t run_range(const fftmv_plan_s *p, int dir, int first, int last, const 
   return e;
 }
 
+// Work is launched on the current device: it must be the plan's.
+bool on_plan_device(const fftmv_plan_s *p) {
+  int d = -1;
+  return hipGetDevice(&d) == hipSuccess && d == p->device;
+}
+
+// The FP64 input [Nt][n_in] and output [Nt][n_out] of one direction overlap.
+bool overlap(const fftmv_plan_s *p, int dir, const double *in, const double *out) {
+  const int64_t n_in = dir == FFTMV_DIR_F ? p->Nm : p->Nd, n_out = dir == FFTMV_DIR_F ? p->Nd : p->Nm;
+  const uintptr_t i0 = reinterpret_cast<uintptr_t>(in), o0 = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t i1 = i0 + static_cast<uintptr_t>(p->Nt * n_in) * sizeof(double);
+  const uintptr_t o1 = o0 + static_cast<uintptr_t>(p->Nt * n_out) * sizeof(double);
+  return i0 < o1 && o0 < i1;
+}
+
 int apply_dir(fftmv_plan_t p, int dir, const double *in, double *out, hipStream_t s) {
   if (!p || !in || !out || !aligned8(in) || !aligned8(out)) return FFTMV_ERR_INVALID_ARG;
-  if (static_cast<const void *>(in) == static_cast<const void *>(out)) return FFTMV_ERR_INVALID_ARG;
+  if (overlap(p, dir, in, out) || !on_plan_device(p)) return FFTMV_ERR_INVALID_ARG;
   try {
     hipError_t e;
     if (p->flags & FFTMV_FLAG_STAGED) {
@@ -661,7 +676,7 @@ int fftmv_query(fftmv_plan_t plan, size_t *fhat_bytes, size_t *workspace_bytes) 
 }
 
 int fftmv_set_mask(fftmv_plan_t plan, uint32_t prec_mask) {
-  if (!plan || (prec_mask & ~FFTMV_PREC_BITS)) return FFTMV_ERR_INVALID_ARG;
+  if (!plan || (prec_mask & ~FFTMV_PREC_BITS) || !on_plan_device(plan)) return FFTMV_ERR_INVALID_ARG;
   if ((needs_fhat32(prec_mask) && !plan->fhat32) || (needs_fhat64(prec_mask) && !plan->fhat64))
     return FFTMV_ERR_INVALID_ARG;
   // Buffers change element type with the mask: clear them so that padding
@@ -682,6 +697,7 @@ int fftmv_run_stages(fftmv_plan_t plan, int dir, int first, int last, const doub
   if (!plan || (dir != 0 && dir != 1) || first < 1 || last > 5 || first > last) return FFTMV_ERR_INVALID_ARG;
   if (first == 1 && (!in || !aligned8(in))) return FFTMV_ERR_INVALID_ARG;
   if (last == 5 && (!out || !aligned8(out))) return FFTMV_ERR_INVALID_ARG;
+  if ((first == 1 && last == 5 && overlap(plan, dir, in, out)) || !on_plan_device(plan)) return FFTMV_ERR_INVALID_ARG;
   try {
     return status_from_hip(run_range(plan, dir, first, last, in, out, stream));
   } catch (...) {
@@ -714,7 +730,7 @@ int fftmv_buffer(fftmv_plan_t plan, int which, void **ptr, int64_t *ld, int *ele
 
 int fftmv_condition(fftmv_plan_t plan, int iters, double *kappa, double *sigma_max, double *sigma_min,
                     hipStream_t stream) {
-  if (!plan) return FFTMV_ERR_INVALID_ARG;
+  if (!plan || !on_plan_device(plan)) return FFTMV_ERR_INVALID_ARG;
   try {
     return condition_impl(plan, iters, kappa, sigma_max, sigma_min, stream);
   } catch (...) {

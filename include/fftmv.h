@@ -42,7 +42,12 @@
  *     tables and one workspace, all in device memory.
  *   - fftmv_apply / fftmv_apply_adjoint are asynchronous on the stream they
  *     are given; they allocate nothing and never synchronise. The caller owns
- *     the vectors and the streams. Outputs must not alias inputs.
+ *     the vectors and the streams. An output that overlaps its input is
+ *     rejected with FFTMV_ERR_INVALID_ARG.
+ *   - A plan lives on the device current at fftmv_setup. Every call that
+ *     launches work with it (applies, fftmv_run_stages, fftmv_set_mask,
+ *     fftmv_condition) needs that device current, else it returns
+ *     FFTMV_ERR_INVALID_ARG without launching anything.
  *   - Applies on one plan share its workspace: they must be ordered (one
  *     stream, or caller synchronisation). Different plans are independent.
  *

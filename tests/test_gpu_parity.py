@@ -284,6 +284,18 @@ def test_error_paths_on_device(fm):
     assert e.value.status == fm.FFTMV_ERR_INVALID_ARG
     with pytest.raises(fm.FftmvError):
         fm.fftmv_apply(plan.handle, c.m_dev.data_ptr(), c.m_dev.data_ptr(), 0)  # aliasing
+    # an output overlapping the tail of the input is rejected; one starting
+    # right after the input's last element is fine
+    Nt, Nm, Nd = 16, 8, 4
+    both = torch.zeros(Nt * Nm + Nt * Nd, dtype=torch.float64, device="cuda")
+    both[: Nt * Nm] = c.m_dev.reshape(-1)
+    torch.cuda.synchronize()
+    with pytest.raises(fm.FftmvError) as e:
+        fm.fftmv_apply(plan.handle, both.data_ptr(), both.data_ptr() + 8 * (Nt * Nm - 3), 0)
+    assert e.value.status == fm.FFTMV_ERR_INVALID_ARG
+    fm.fftmv_apply(plan.handle, both.data_ptr(), both.data_ptr() + 8 * Nt * Nm, 0)
+    v_ref = host(plan.apply(c.m_dev))
+    assert np.array_equal(host(both[Nt * Nm:]).reshape(Nt, Nd), v_ref)
     fh, ws = plan.query()
     assert fh == 17 * 4 * plan.buffer_info(0)[1] * 8 and ws > 0
     plan.close()
