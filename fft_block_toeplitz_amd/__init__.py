@@ -268,6 +268,14 @@ class Plan:
         self.mask = mask
 
     def run_stages(self, direction: int, first: int, last: int, x=None, out=None, stream=None) -> None:
+        """Stages first..last of one direction: x (the FP64 input, needed when
+        first == 1) and out (the FP64 output, when last == 5) are checked
+        against the direction's shapes."""
+        n_in, n_out = (self.Nm, self.Nd) if direction == FFTMV_DIR_F else (self.Nd, self.Nm)
+        if first == 1:
+            _require(x, (self.Nt, n_in), "x")
+        if last == 5:
+            _require(out, (self.Nt, n_out), "out")
         fftmv_run_stages(self.handle, direction, first, last, None if x is None else x.data_ptr(),
                          None if out is None else out.data_ptr(), _stream_handle(stream))
 
