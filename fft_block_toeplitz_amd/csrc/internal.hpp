@@ -121,6 +121,10 @@ struct SbgemvArgs {
   void *y = nullptr;        // output [K][ldy] complex (float if y_f32)
   int64_t ldy = 0;
   bool y_f32 = false;
+  // F* only: workspace of the tall-block form (partial column sums per row
+  // segment), part_bytes long; null keeps the short-wide kernel
+  void *part = nullptr;
+  size_t part_bytes = 0;
 };
 
 // Real [rows][cols] copy with precision change: dst[r*ldd+c] = src[r*lds+c].
@@ -160,6 +164,9 @@ bool launch_fft_inverse_fixed(const FftGeom &g, const InvFftArgs &a, bool comput
                               hipStream_t s);
 hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s);
 hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s);
+// Bytes of the F* tall-block workspace for this shape (the larger of the two
+// compute precisions); 0 when neither uses the tall-block form.
+size_t sbgemv_c_part_bytes(int64_t K, int64_t Nd, int64_t Nm);
 hipError_t launch_cast(const CastArgs &a, hipStream_t s);
 
 // Lanczos process on the per-frequency Gram matrices (condition.hip). One

@@ -39,6 +39,8 @@ struct fftmv_plan_s {
   int64_t ldF32 = 0, ldF64 = 0;
   void *tw32 = nullptr, *tw64 = nullptr;
   StageBuf buf[2][5];
+  void *part = nullptr;  // F* tall-block workspace (partial column sums), part_bytes long
+  size_t part_bytes = 0;
   size_t fhat_bytes = 0, ws_bytes = 0;
   void *allocs[16] = {};
   int nalloc = 0;
@@ -238,6 +240,8 @@ hipError_t stage_sbgemv(const fftmv_plan_s *p, int dir, hipStream_t s) {
   a.y = p->buf[dir][3].p;
   a.ldy = p->buf[dir][3].ld;
   a.y_f32 = buf_f32(p->prec, dir, 3);
+  a.part = p->part;
+  a.part_bytes = p->part_bytes;
   if (!a.F) return hipErrorInvalidValue;
   return dir == 0 ? launch_sbgemv_n(a, cf32, s) : launch_sbgemv_c(a, cf32, s);
 }
@@ -441,6 +445,14 @@ int setup_impl(fftmv_plan_s *p, const double *F, hipStream_t s) {
       p->buf[dir][st].ld = lds[st];
       p->ws_bytes += static_cast<size_t>(bytes);
     }
+  }
+
+  // partial column sums of the tall-block F* product (blocks with few
+  // columns and many rows), for either compute precision
+  p->part_bytes = sbgemv_c_part_bytes(K, Nd, Nm);
+  if (p->part_bytes) {
+    FFTMV_TRY(dev_alloc(p, &p->part, p->part_bytes));
+    p->ws_bytes += p->part_bytes;
   }
 
   // Fhat_k = DFT of every zero-padded (r, c) series, computed in FP64 and

@@ -295,6 +295,84 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
   }
 }
 
+// ------------------------------------------------------- F*, tall blocks
+// w_k[c] = sum_r conj(Fhat_k[r][c]) d_k[r] when a block has few columns
+// (nvec <= 128 16-byte vectors) and many rows: the short-wide kernel would
+// leave most lanes idle and walk all Nd rows one load at a time. Here thread
+// t of a workgroup takes column vector j = t % nvec and rows q, q + P, ...
+// (q = t / nvec, P = 256 / nvec rows per step) of one segment of rows, so a
+// step loads P rows x nvec vectors; the P partial sums of each column are
+// added in LDS in row-slot order and written per (frequency, segment); a
+// second kernel adds the segments in order. Fixed orders throughout, so the
+// result is bitwise repeatable.
+template <typename T, typename In>
+__global__ __launch_bounds__(kBlock) void sbgemv_c_tall_kernel(const typename Vec16<T>::type *__restrict__ F,
+                                                               const cx<In> *__restrict__ x, cx<T> *__restrict__ part,
+                                                               int64_t Nd, int64_t ldF_vec, int64_t nvec, int64_t ldx,
+                                                               int64_t nseg, int64_t seg_rows, int64_t nblocks) {
+  using V = typename Vec16<T>::type;
+  constexpr int NV = Vec16<T>::n;
+  __shared__ cx<T> red[kBlock * NV];
+  const int64_t blk = xcd_contiguous_block(blockIdx.x, nblocks);
+  const int64_t k = blk / nseg, seg = blk - k * nseg;
+  const int nv = static_cast<int>(nvec);
+  const int P = kBlock / nv;
+  const int t = threadIdx.x, q = t / nv, j = t - q * nv;
+  T ar[NV], ai[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) ar[e] = ai[e] = T(0);
+  if (q < P) {
+    const int64_t r1 = (seg + 1) * seg_rows < Nd ? (seg + 1) * seg_rows : Nd;
+    const V *col = F + k * Nd * ldF_vec + j;
+    const cx<In> *xk = x + k * ldx;
+#pragma unroll 4
+    for (int64_t r = seg * seg_rows + q; r < r1; r += P) {
+      const cx<T> d = cvt<T>(xk[r]);
+      cx<T> f[NV];
+      split(__builtin_nontemporal_load(col + r * ldF_vec), f);
+#pragma unroll
+      for (int e = 0; e < NV; ++e) fma_conj_mul(ar[e], ai[e], f[e], d);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < NV; ++e) red[t * NV + e] = mk(ar[e], ai[e]);
+  __syncthreads();
+  if (t < nv) {
+    cx<T> acc[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) acc[e] = red[t * NV + e];
+    for (int qq = 1; qq < P; ++qq)
+#pragma unroll
+      for (int e = 0; e < NV; ++e) {
+        const cx<T> v = red[(qq * nv + t) * NV + e];
+        acc[e] = mk(acc[e].re + v.re, acc[e].im + v.im);
+      }
+#pragma unroll
+    for (int e = 0; e < NV; ++e) part[((k * nseg + seg) * nvec + t) * NV + e] = acc[e];
+  }
+}
+
+// Segment sums of the tall-block form, in segment order, into w_k.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void sbgemv_c_tall_reduce_kernel(const cx<T> *__restrict__ part, void *y,
+                                                                      int64_t K, int64_t nseg, int64_t nvec,
+                                                                      int64_t ldy, bool y_f32) {
+  constexpr int NV = Vec16<T>::n;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i >= K * nvec) return;
+  const int64_t k = i / nvec, j = i - k * nvec;
+  cx<T> acc[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) acc[e] = part[((k * nseg) * nvec + j) * NV + e];
+  for (int64_t sg = 1; sg < nseg; ++sg)
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const cx<T> v = part[((k * nseg + sg) * nvec + j) * NV + e];
+      acc[e] = mk(acc[e].re + v.re, acc[e].im + v.im);
+    }
+  store_vec(y, k * ldy + j * NV, y_f32, acc);
+}
+
 constexpr int kRowsN = 4;    // rows per wave, F direction
 constexpr int kUnrollN = 2;  // vectors per row in flight, F direction
 constexpr int kChainsN = 4;  // partial sums per row and lane, F direction
@@ -377,6 +455,51 @@ void launch_c_vl(const SbgemvArgs &a, int64_t nvec, hipStream_t s) {
   }
 }
 
+// The tall-block form of F*: used when a block has at most 128 column
+// vectors (two rows per step at least) and at least kTallMinRows rows.
+// Segments of rows give at least kTallMinBlocks workgroups when the rows
+// allow it, each thread keeping at least kTallMinPerThread rows.
+constexpr int64_t kTallMaxVecs = kBlock / 2;
+constexpr int64_t kTallMinRows = 64;
+constexpr int64_t kTallMinBlocks = 4096;
+constexpr int64_t kTallMinPerThread = 8;
+
+struct TallSplit {
+  int64_t nseg = 0, seg_rows = 0;  // nseg == 0: not the tall-block form
+};
+
+TallSplit tall_split(int64_t K, int64_t Nd, int64_t nvec) {
+  TallSplit ts;
+  if (nvec > kTallMaxVecs || Nd < kTallMinRows || K < 1) return ts;
+  const int64_t P = kBlock / nvec;
+  int64_t max_seg = Nd / (P * kTallMinPerThread);
+  max_seg = max_seg < 1 ? 1 : max_seg;
+  int64_t want = (kTallMinBlocks + K - 1) / K;
+  want = want < 1 ? 1 : want;
+  const int64_t nseg0 = want < max_seg ? want : max_seg;
+  ts.seg_rows = (Nd + nseg0 - 1) / nseg0;
+  ts.nseg = (Nd + ts.seg_rows - 1) / ts.seg_rows;
+  return ts;
+}
+
+size_t tall_part_bytes(int64_t K, int64_t nvec, const TallSplit &ts) {
+  return static_cast<size_t>(K * ts.nseg * nvec) * 16;  // one 16-byte vector per (k, segment, column vector)
+}
+
+template <typename T, typename In>
+void launch_c_tall(const SbgemvArgs &a, int64_t nvec, const TallSplit &ts, hipStream_t s) {
+  using V = typename Vec16<T>::type;
+  const int nv = Vec16<T>::n;
+  const int64_t nblocks = a.K * ts.nseg;
+  cx<T> *part = static_cast<cx<T> *>(a.part);
+  hipLaunchKernelGGL((sbgemv_c_tall_kernel<T, In>), dim3(static_cast<unsigned>(nblocks)), dim3(kBlock), 0, s,
+                     static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), part, a.Nd, a.ldF / nv, nvec,
+                     a.ldx, ts.nseg, ts.seg_rows, nblocks);
+  const int64_t nred = (a.K * nvec + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL((sbgemv_c_tall_reduce_kernel<T>), dim3(static_cast<unsigned>(nred)), dim3(kBlock), 0, s, part,
+                     a.y, a.K, ts.nseg, nvec, a.ldy, a.y_f32);
+}
+
 }  // namespace
 
 hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s) {
@@ -406,6 +529,17 @@ hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
 hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s) {
   const int nv = compute_f32 ? 2 : 1;
   const int64_t nvec = (a.Nm + nv - 1) / nv;
+  const TallSplit ts = tall_split(a.K, a.Nd, nvec);
+  const size_t need = ts.nseg ? tall_part_bytes(a.K, nvec, ts) : 0;
+  if (need && a.part && a.part_bytes >= need) {
+    if (compute_f32)
+      launch_c_tall<float, float>(a, nvec, ts, s);
+    else if (a.x_f32)
+      launch_c_tall<double, float>(a, nvec, ts, s);
+    else
+      launch_c_tall<double, double>(a, nvec, ts, s);
+    return hipGetLastError();
+  }
   if (compute_f32)
     launch_c_vl<float, float>(a, nvec, s);
   else if (a.x_f32)
@@ -413,6 +547,19 @@ hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
   else
     launch_c_vl<double, double>(a, nvec, s);
   return hipGetLastError();
+}
+
+size_t sbgemv_c_part_bytes(int64_t K, int64_t Nd, int64_t Nm) {
+  size_t bytes = 0;
+  for (int nv = 1; nv <= 2; ++nv) {
+    const int64_t nvec = (Nm + nv - 1) / nv;
+    const TallSplit ts = tall_split(K, Nd, nvec);
+    if (ts.nseg) {
+      const size_t b = tall_part_bytes(K, nvec, ts);
+      bytes = b > bytes ? b : bytes;
+    }
+  }
+  return bytes;
 }
 
 }  // namespace fftmv

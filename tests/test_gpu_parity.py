@@ -93,6 +93,9 @@ SHAPES = [
     (4103, 3, 1000), # wide batches (8-channel tiles, ragged last tile) at Main's length
     (700, 3, 1000),  # the smallest wide batches (from 512 channels), ragged last tile
     (3, 600, 1000),  # wide batches on the F* forward and F inverse side
+    (5, 4000, 8),    # tall blocks: the F* product in 5 (FP32) / 9 (FP64) row segments
+    (64, 200, 100),  # tall blocks, 32 / 64 column vectors, 3 / 6 segments
+    (256, 64, 16),   # 128 column vectors in FP32: the widest tall-block case
     (513, 2, 2000),  # wide batch at the Scale share's length, one channel in the last tile
     (33, 7, 2000),   # the Scale share's time length, narrow batches
     (3, 2, 4096),    # the longest supported transform, 2Nt = 2^13
