@@ -211,6 +211,51 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   }
 }
 
+// ----------------------------------------------------------- F, narrow rows
+// v_k[r] = sum_c Fhat_k[r][c] m_k[c] when rows have at most 32 16-byte
+// vectors: the wave-per-four-rows kernel would leave most lanes idle. Thread
+// t takes column vector j = t % G of row slot q = t / G (G the power of two
+// >= nvec, P = 256 / G row slots per workgroup), keeps m_k's vector j in
+// registers and walks rows q, q + P, ... of its workgroup's row segment; the
+// G lanes of a row add their products with a butterfly in a fixed order.
+template <typename T, typename In, int G>
+__global__ __launch_bounds__(kBlock) void sbgemv_n_narrow_kernel(const typename Vec16<T>::type *__restrict__ F,
+                                                                 const cx<In> *__restrict__ x, void *__restrict__ y,
+                                                                 int64_t Nd, int64_t ldF_vec, int64_t nvec,
+                                                                 int64_t ldx, int64_t ldy, bool y_f32, int64_t nseg,
+                                                                 int64_t seg_rows, int64_t nblocks) {
+  using V = typename Vec16<T>::type;
+  constexpr int NV = Vec16<T>::n;
+  constexpr int P = kBlock / G;
+  const int64_t blk = xcd_contiguous_block(blockIdx.x, nblocks);
+  const int64_t k = blk / nseg, seg = blk - k * nseg;
+  const int t = threadIdx.x, q = t / G, j = t % G;
+  const bool live = j < nvec;
+  cx<T> xv[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) xv[e] = mk(T(0), T(0));
+  if (live) load_x<T, In>(x + k * ldx, j, xv);
+  const int64_t r1 = (seg + 1) * seg_rows < Nd ? (seg + 1) * seg_rows : Nd;
+  const V *col = F + k * Nd * ldF_vec + (live ? j : 0);
+  // the G lanes of one row share q, so they run the same iterations
+#pragma unroll 4
+  for (int64_t r = seg * seg_rows + q; r < r1; r += P) {
+    T re = T(0), im = T(0);
+    if (live) {
+      cx<T> f[NV];
+      split(__builtin_nontemporal_load(col + r * ldF_vec), f);
+#pragma unroll
+      for (int e = 0; e < NV; ++e) fma_mul(re, im, f[e], xv[e]);
+    }
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) {
+      re += __shfl_xor(re, m);
+      im += __shfl_xor(im, m);
+    }
+    if (j == 0) store_y(y, k * ldy + r, y_f32, mk(re, im));
+  }
+}
+
 // ------------------------------------------------------------------ F*
 // w_k[c] = sum_r conj(Fhat_k[r][c]) d_k[r].
 // One workgroup per (frequency k, chunk of VL*256 consecutive 16-byte column
@@ -500,11 +545,70 @@ void launch_c_tall(const SbgemvArgs &a, int64_t nvec, const TallSplit &ts, hipSt
                      a.y, a.K, ts.nseg, nvec, a.ldy, a.y_f32);
 }
 
+// The narrow-row form of F: rows of at most kNarrowMaxVecs vectors, in
+// segments that give at least kTallMinBlocks workgroups when the rows allow
+// it, each thread keeping at least kTallMinPerThread rows.
+constexpr int64_t kNarrowMaxVecs = 32;
+
+struct NarrowSplit {
+  int G = 0;  // 0: not the narrow-row form
+  int64_t nseg = 0, seg_rows = 0;
+};
+
+NarrowSplit narrow_split(int64_t K, int64_t Nd, int64_t nvec) {
+  NarrowSplit ns;
+  if (nvec > kNarrowMaxVecs || K < 1 || Nd < 1) return ns;
+  int G = 1;
+  while (G < nvec) G <<= 1;
+  const int64_t P = kBlock / G;
+  int64_t max_seg = Nd / (P * kTallMinPerThread);
+  max_seg = max_seg < 1 ? 1 : max_seg;
+  int64_t want = (kTallMinBlocks + K - 1) / K;
+  want = want < 1 ? 1 : want;
+  const int64_t nseg0 = want < max_seg ? want : max_seg;
+  ns.G = G;
+  ns.seg_rows = (Nd + nseg0 - 1) / nseg0;
+  ns.nseg = (Nd + ns.seg_rows - 1) / ns.seg_rows;
+  return ns;
+}
+
+template <typename T, typename In, int G>
+void launch_n_narrow_g(const SbgemvArgs &a, int64_t nvec, const NarrowSplit &ns, hipStream_t s) {
+  using V = typename Vec16<T>::type;
+  const int nv = Vec16<T>::n;
+  const int64_t nblocks = a.K * ns.nseg;
+  hipLaunchKernelGGL((sbgemv_n_narrow_kernel<T, In, G>), dim3(static_cast<unsigned>(nblocks)), dim3(kBlock), 0, s,
+                     static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd, a.ldF / nv, nvec,
+                     a.ldx, a.ldy, a.y_f32, ns.nseg, ns.seg_rows, nblocks);
+}
+
+template <typename T, typename In>
+void launch_n_narrow(const SbgemvArgs &a, int64_t nvec, const NarrowSplit &ns, hipStream_t s) {
+  switch (ns.G) {
+    case 1: launch_n_narrow_g<T, In, 1>(a, nvec, ns, s); break;
+    case 2: launch_n_narrow_g<T, In, 2>(a, nvec, ns, s); break;
+    case 4: launch_n_narrow_g<T, In, 4>(a, nvec, ns, s); break;
+    case 8: launch_n_narrow_g<T, In, 8>(a, nvec, ns, s); break;
+    case 16: launch_n_narrow_g<T, In, 16>(a, nvec, ns, s); break;
+    default: launch_n_narrow_g<T, In, 32>(a, nvec, ns, s); break;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s) {
   const int nv = compute_f32 ? 2 : 1;
   const int64_t nvec = (a.Nm + nv - 1) / nv;
+  const NarrowSplit ns = narrow_split(a.K, a.Nd, nvec);
+  if (ns.G) {
+    if (compute_f32)
+      launch_n_narrow<float, float>(a, nvec, ns, s);
+    else if (a.x_f32)
+      launch_n_narrow<double, float>(a, nvec, ns, s);
+    else
+      launch_n_narrow<double, double>(a, nvec, ns, s);
+    return hipGetLastError();
+  }
   const int64_t ngroups = (a.Nd + kRowsN - 1) / kRowsN;
   const int64_t ntasks = a.K * ngroups;
   const int64_t nblocks = (ntasks + (kBlock / kWave) - 1) / (kBlock / kWave);
