@@ -275,12 +275,16 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_narrow_kernel(const typename 
 template <typename T, typename In, int VL, int U>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void sbgemv_c_kernel(
     const typename Vec16<T>::type *__restrict__ F, const cx<In> *__restrict__ x, void *__restrict__ y, int64_t Nd,
-    int64_t ldF_vec, int64_t nvec, int64_t ldx, int64_t ldy, bool y_f32, int64_t nchunks, int64_t nblocks) {
+    int64_t ldF_vec, int64_t nvec, int64_t ldx, int64_t ldy, bool y_f32, int64_t nchunks, int64_t nblocks,
+    cx<T> *__restrict__ part, int64_t nseg, int64_t seg_rows) {
   using V = typename Vec16<T>::type;
   constexpr int NV = Vec16<T>::n;
   const int64_t blk = xcd_contiguous_block(blockIdx.x, nblocks);
-  const int64_t k = blk / nchunks;
-  const int64_t j0 = (blk - k * nchunks) * (kBlock * VL) + threadIdx.x;
+  // tile (k, chunk), then its row segment (nseg == 1: all Nd rows, into y)
+  const int64_t tile = nseg == 1 ? blk : blk / nseg, seg = blk - tile * nseg;
+  const int64_t k = tile / nchunks;
+  const int64_t j0 = (tile - k * nchunks) * (kBlock * VL) + threadIdx.x;
+  const int64_t r_end = (seg + 1) * seg_rows < Nd ? (seg + 1) * seg_rows : Nd;
   const V *base = F + k * Nd * ldF_vec;
   const cx<In> *xk = x + k * ldx;
   uint32_t off[VL];  // byte offsets within a row (rows are far below 4 GiB)
@@ -298,8 +302,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
     for (int e = 0; e < NV; ++e) ar[v][e] = ai[v][e] = T(0);
 
   const int64_t row_bytes = nvec * static_cast<int64_t>(sizeof(V));
-  int64_t r = 0;
-  for (; r + U <= Nd; r += U) {
+  int64_t r = seg * seg_rows;
+  for (; r + U <= r_end; r += U) {
     cx<T> d[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) d[u] = cvt<T>(xk[r + u]);
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
       }
     }
   }
-  for (; r < Nd; ++r) {  // fewer than U rows left
+  for (; r < r_end; ++r) {  // fewer than U rows left
     const cx<T> d = cvt<T>(xk[r]);
     const __amdgpu_buffer_rsrc_t rs = row_rsrc(base + r * ldF_vec, row_bytes);
 #pragma unroll
@@ -335,7 +339,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
       cx<T> out[NV];
 #pragma unroll
       for (int e = 0; e < NV; ++e) out[e] = mk(ar[v][e], ai[v][e]);
-      store_vec(y, k * ldy + j * NV, y_f32, out);
+      if (nseg == 1) {
+        store_vec(y, k * ldy + j * NV, y_f32, out);
+      } else {
+#pragma unroll
+        for (int e = 0; e < NV; ++e) part[((k * nseg + seg) * nvec + j) * NV + e] = out[e];
+      }
     }
   }
 }
@@ -397,9 +406,10 @@ __global__ __launch_bounds__(kBlock) void sbgemv_c_tall_kernel(const typename Ve
   }
 }
 
-// Segment sums of the tall-block form, in segment order, into w_k.
+// Segment sums (tall-block form, or row segments of the short-wide kernel),
+// in segment order, into w_k.
 template <typename T>
-__global__ __launch_bounds__(kBlock) void sbgemv_c_tall_reduce_kernel(const cx<T> *__restrict__ part, void *y,
+__global__ __launch_bounds__(kBlock) void sbgemv_c_reduce_kernel(const cx<T> *__restrict__ part, void *y,
                                                                       int64_t K, int64_t nseg, int64_t nvec,
                                                                       int64_t ldy, bool y_f32) {
   constexpr int NV = Vec16<T>::n;
@@ -426,13 +436,19 @@ constexpr int kMaxVecsC = 5;  // vectors per lane, F* direction (at most)
 constexpr int kUnrollC = 2;   // rows per step (one scalar load of d_k), F* direction
 
 template <typename T, typename In, int VL>
-void launch_c(const SbgemvArgs &a, int64_t nvec, int64_t nchunks, hipStream_t s) {
+void launch_c(const SbgemvArgs &a, int64_t nvec, int64_t nchunks, int64_t nseg, int64_t seg_rows, hipStream_t s) {
   using V = typename Vec16<T>::type;
   const int nv = Vec16<T>::n;
-  const int64_t nblocks = a.K * nchunks;
+  const int64_t nblocks = a.K * nchunks * nseg;
+  cx<T> *part = static_cast<cx<T> *>(a.part);
   hipLaunchKernelGGL((sbgemv_c_kernel<T, In, VL, kUnrollC>), dim3(static_cast<unsigned>(nblocks)),
                      dim3(kBlock), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
-                     a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks);
+                     a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks, part, nseg, seg_rows);
+  if (nseg > 1) {
+    const int64_t nred = (a.K * nvec + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL((sbgemv_c_reduce_kernel<T>), dim3(static_cast<unsigned>(nred)), dim3(kBlock), 0, s, part,
+                       a.y, a.K, nseg, nvec, a.ldy, a.y_f32);
+  }
 }
 
 // Workgroups of the conjugate-transpose kernel that one CU holds at once:
@@ -488,15 +504,50 @@ ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots) {
   return best;
 }
 
+// Row segments of the short-wide kernel: when its tiles fill less than half
+// a round of resident workgroups, each tile walks all Nd rows one load at a
+// time while most of the GPU idles (few frequencies and many rows, e.g.
+// Nt = 256 with Nd = 4000). The rows are then split into nseg segments (at
+// most slots / tiles of them, at least kSegMinRows rows each); each
+// workgroup stores its segment's partial sums in the plan workspace and a
+// second kernel adds the segments in order.
+constexpr int64_t kSegMinRows = 64;
+
+struct SegC {
+  int64_t nseg = 1, seg_rows = 0;
+};
+
+SegC seg_c(int64_t K, int64_t nchunks, int64_t Nd, int64_t slots) {
+  SegC sc;
+  sc.seg_rows = Nd;
+  int64_t n = slots / (K * nchunks);
+  const int64_t by_rows = Nd / kSegMinRows;
+  n = n < by_rows ? n : by_rows;
+  if (n < 2) return sc;
+  sc.seg_rows = (Nd + n - 1) / n;
+  sc.nseg = (Nd + sc.seg_rows - 1) / sc.seg_rows;
+  return sc;
+}
+
+size_t seg_part_bytes(int64_t K, int64_t nvec, const SegC &sc) {
+  return sc.nseg > 1 ? static_cast<size_t>(K * sc.nseg * nvec) * 16 : 0;
+}
+
 template <typename T, typename In>
 void launch_c_vl(const SbgemvArgs &a, int64_t nvec, hipStream_t s) {
-  const ChunksC c = choose_chunks_c(a.K, nvec, resident_c_workgroups());
+  const int64_t slots = resident_c_workgroups();
+  const ChunksC c = choose_chunks_c(a.K, nvec, slots);
+  SegC sc = seg_c(a.K, c.nchunks, a.Nd, slots);
+  if (sc.nseg > 1 && !(a.part && a.part_bytes >= seg_part_bytes(a.K, nvec, sc))) {
+    sc.nseg = 1;  // no workspace (callers outside an apply): all rows in one pass
+    sc.seg_rows = a.Nd;
+  }
   switch (c.vl) {
-    case 1: launch_c<T, In, 1>(a, nvec, c.nchunks, s); break;
-    case 2: launch_c<T, In, 2>(a, nvec, c.nchunks, s); break;
-    case 3: launch_c<T, In, 3>(a, nvec, c.nchunks, s); break;
-    case 4: launch_c<T, In, 4>(a, nvec, c.nchunks, s); break;
-    default: launch_c<T, In, 5>(a, nvec, c.nchunks, s); break;
+    case 1: launch_c<T, In, 1>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s); break;
+    case 2: launch_c<T, In, 2>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s); break;
+    case 3: launch_c<T, In, 3>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s); break;
+    case 4: launch_c<T, In, 4>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s); break;
+    default: launch_c<T, In, 5>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s); break;
   }
 }
 
@@ -541,7 +592,7 @@ void launch_c_tall(const SbgemvArgs &a, int64_t nvec, const TallSplit &ts, hipSt
                      static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), part, a.Nd, a.ldF / nv, nvec,
                      a.ldx, ts.nseg, ts.seg_rows, nblocks);
   const int64_t nred = (a.K * nvec + kBlock - 1) / kBlock;
-  hipLaunchKernelGGL((sbgemv_c_tall_reduce_kernel<T>), dim3(static_cast<unsigned>(nred)), dim3(kBlock), 0, s, part,
+  hipLaunchKernelGGL((sbgemv_c_reduce_kernel<T>), dim3(static_cast<unsigned>(nred)), dim3(kBlock), 0, s, part,
                      a.y, a.K, ts.nseg, nvec, a.ldy, a.y_f32);
 }
 
@@ -654,14 +705,19 @@ hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
 }
 
 size_t sbgemv_c_part_bytes(int64_t K, int64_t Nd, int64_t Nm) {
+  const int64_t slots = resident_c_workgroups();
   size_t bytes = 0;
   for (int nv = 1; nv <= 2; ++nv) {
     const int64_t nvec = (Nm + nv - 1) / nv;
     const TallSplit ts = tall_split(K, Nd, nvec);
+    size_t b = 0;
     if (ts.nseg) {
-      const size_t b = tall_part_bytes(K, nvec, ts);
-      bytes = b > bytes ? b : bytes;
+      b = tall_part_bytes(K, nvec, ts);
+    } else {
+      const ChunksC c = choose_chunks_c(K, nvec, slots);
+      b = seg_part_bytes(K, nvec, seg_c(K, c.nchunks, Nd, slots));
     }
+    bytes = b > bytes ? b : bytes;
   }
   return bytes;
 }
