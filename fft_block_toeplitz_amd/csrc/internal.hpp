@@ -121,8 +121,8 @@ struct SbgemvArgs {
   void *y = nullptr;        // output [K][ldy] complex (float if y_f32)
   int64_t ldy = 0;
   bool y_f32 = false;
-  // F* only: workspace of the tall-block form (partial column sums per row
-  // segment), part_bytes long; null keeps the short-wide kernel
+  // workspace for partial sums (F* tall blocks and row segments, F column
+  // chunks), part_bytes long; null keeps the one-pass kernels
   void *part = nullptr;
   size_t part_bytes = 0;
 };
@@ -164,9 +164,10 @@ bool launch_fft_inverse_fixed(const FftGeom &g, const InvFftArgs &a, bool comput
                               hipStream_t s);
 hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s);
 hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s);
-// Bytes of the F* tall-block workspace for this shape (the larger of the two
-// compute precisions); 0 when neither uses the tall-block form.
-size_t sbgemv_c_part_bytes(int64_t K, int64_t Nd, int64_t Nm);
+// Bytes of the GEMV workspace for this shape: partial sums of the F*
+// tall-block form and row segments, and of the F column chunks (the largest
+// over both directions and compute precisions); 0 when no launch needs it.
+size_t sbgemv_part_bytes(int64_t K, int64_t Nd, int64_t Nm);
 hipError_t launch_cast(const CastArgs &a, hipStream_t s);
 
 // Lanczos process on the per-frequency Gram matrices (condition.hip). One

@@ -39,7 +39,7 @@ struct fftmv_plan_s {
   int64_t ldF32 = 0, ldF64 = 0;
   void *tw32 = nullptr, *tw64 = nullptr;
   StageBuf buf[2][5];
-  void *part = nullptr;  // F* tall-block workspace (partial column sums), part_bytes long
+  void *part = nullptr;  // GEMV partial sums (F* tall blocks / row segments, F column chunks)
   size_t part_bytes = 0;
   size_t fhat_bytes = 0, ws_bytes = 0;
   void *allocs[16] = {};
@@ -447,9 +447,9 @@ int setup_impl(fftmv_plan_s *p, const double *F, hipStream_t s) {
     }
   }
 
-  // partial column sums of the tall-block F* product (blocks with few
-  // columns and many rows), for either compute precision
-  p->part_bytes = sbgemv_c_part_bytes(K, Nd, Nm);
+  // partial sums of the GEMV forms that split a frequency's work (F*: tall
+  // blocks and row segments; F: column chunks), for either precision
+  p->part_bytes = sbgemv_part_bytes(K, Nd, Nm);
   if (p->part_bytes) {
     FFTMV_TRY(dev_alloc(p, &p->part, p->part_bytes));
     p->ws_bytes += p->part_bytes;

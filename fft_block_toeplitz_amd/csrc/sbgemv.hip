@@ -134,7 +134,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE, WPE
                                                           const cx<In> *__restrict__ x, void *__restrict__ y,
                                                           int64_t Nd, int64_t ldF_vec, int64_t nvec, int64_t ldx,
                                                           int64_t ldy, bool y_f32, int64_t ngroups, int64_t ntasks,
-                                                          int64_t nblocks) {
+                                                          int64_t nblocks, cx<T> *__restrict__ part, int64_t ncc,
+                                                          int64_t cc_len) {
   using V = typename Vec16<T>::type;
   constexpr int NV = Vec16<T>::n;
   constexpr int NC = U * NV < NCH ? U * NV : NCH;  // chains per row and lane
@@ -144,8 +145,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t task = xcd_contiguous_block(blockIdx.x, nblocks) * (kBlock / kWave) + wave;
   if (task >= ntasks) return;
-  const int64_t k = task / ngroups;
-  const int64_t r0 = (task - k * ngroups) * R;
+  // (frequency, row group), then its column chunk (ncc == 1: whole rows, into y)
+  const int64_t kg = ncc == 1 ? task : task / ncc, cc = task - kg * ncc;
+  const int64_t k = kg / ngroups;
+  const int64_t r0 = (kg - k * ngroups) * R;
+  const int64_t c1 = (cc + 1) * cc_len < nvec ? (cc + 1) * cc_len : nvec;
 
   // one buffer descriptor per row (scalar registers): a load is the row's
   // descriptor plus the lane's 32-bit offset, shared by all R rows
@@ -163,8 +167,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE, WPE
 #pragma unroll
     for (int c = 0; c < NC; ++c) ar[i][c] = ai[i][c] = T(0);
 
-  int64_t j = lane;
-  for (; j + (U - 1) * kWave < nvec; j += U * kWave) {
+  int64_t j = cc * cc_len + lane;
+  for (; j + (U - 1) * kWave < c1; j += U * kWave) {
     V fv[U][R];
     cx<T> xv[U][NV];
 #pragma unroll
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE, WPE
         for (int e = 0; e < NV; ++e) fma_mul(ar[i][(u * NV + e) % NC], ai[i][(u * NV + e) % NC], f[e], xv[u][e]);
       }
   }
-  for (; j < nvec; j += kWave) {  // fewer than U vectors left in the row
+  for (; j < c1; j += kWave) {  // fewer than U vectors left in the chunk
     cx<T> xv[NV];
     load_x<T, In>(xk, j, xv);
 #pragma unroll
@@ -207,8 +211,28 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE, WPE
         ai[i][q] += ai[i][q + w];
       }
     cx<T> s = mk(wave_sum(ar[i][0]), wave_sum(ai[i][0]));
-    if (lane == 0 && r0 + i < Nd) store_y(y, k * ldy + r0 + i, y_f32, s);
+    if (lane == 0 && r0 + i < Nd) {
+      if (ncc == 1)
+        store_y(y, k * ldy + r0 + i, y_f32, s);
+      else
+        part[(k * ncc + cc) * Nd + r0 + i] = s;
+    }
   }
+}
+
+// Column-chunk sums of the wide-row F kernel, in chunk order, into v_k.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void sbgemv_n_reduce_kernel(const cx<T> *__restrict__ part, void *y, int64_t K,
+                                                                 int64_t Nd, int64_t ncc, int64_t ldy, bool y_f32) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i >= K * Nd) return;
+  const int64_t k = i / Nd, r = i - k * Nd;
+  cx<T> acc = part[(k * ncc) * Nd + r];
+  for (int64_t c = 1; c < ncc; ++c) {
+    const cx<T> v = part[(k * ncc + c) * Nd + r];
+    acc = mk(acc.re + v.re, acc.im + v.im);
+  }
+  store_y(y, k * ldy + r, y_f32, acc);
 }
 
 // ----------------------------------------------------------- F, narrow rows
@@ -645,6 +669,61 @@ void launch_n_narrow(const SbgemvArgs &a, int64_t nvec, const NarrowSplit &ns, h
   }
 }
 
+// Column chunks of the wide-row F kernel: with fewer waves (frequencies x
+// row groups) than half the resident wave slots, each wave would stream
+// whole rows alone (few frequencies, few rows, long rows). The rows are
+// then cut into ncc chunks (at most slots / waves, each at least
+// kMinChunkVecsN vectors and a multiple of one step of the wave loop, so
+// every load stays a contiguous 1 KiB); each wave stores its chunk's sums
+// in the plan workspace and a second kernel adds the chunks in order.
+constexpr int64_t kMinChunkVecsN = kWave * kUnrollN * 8;
+
+struct ColN {
+  int64_t ncc = 1, cc_len = 0;
+};
+
+int64_t resident_n_waves() { return static_cast<int64_t>(resident_c_workgroups()) / kResidentPerCuC * 4 * kWavesN; }
+
+ColN col_n(int64_t K, int64_t Nd, int64_t nvec, int64_t wave_slots) {
+  ColN cn;
+  cn.cc_len = nvec;
+  const int64_t waves = K * ((Nd + kRowsN - 1) / kRowsN);
+  int64_t n = wave_slots / waves;
+  const int64_t by_len = nvec / kMinChunkVecsN;
+  n = n < by_len ? n : by_len;
+  if (n < 2) return cn;
+  constexpr int64_t step = kWave * kUnrollN;
+  cn.cc_len = ((nvec + n - 1) / n + step - 1) / step * step;
+  cn.ncc = (nvec + cn.cc_len - 1) / cn.cc_len;
+  if (cn.ncc < 2) {
+    cn.ncc = 1;
+    cn.cc_len = nvec;
+  }
+  return cn;
+}
+
+size_t col_part_bytes(int64_t K, int64_t Nd, const ColN &cn) {
+  return cn.ncc > 1 ? static_cast<size_t>(K * cn.ncc * Nd) * 16 : 0;  // one complex (<= 16 bytes) per row and chunk
+}
+
+template <typename T, typename In>
+void launch_n_wide(const SbgemvArgs &a, int64_t nvec, const ColN &cn, hipStream_t s) {
+  using V = typename Vec16<T>::type;
+  const int nv = Vec16<T>::n;
+  const int64_t ngroups = (a.Nd + kRowsN - 1) / kRowsN;
+  const int64_t ntasks = a.K * ngroups * cn.ncc;
+  const int64_t nblocks = (ntasks + (kBlock / kWave) - 1) / (kBlock / kWave);
+  cx<T> *part = static_cast<cx<T> *>(a.part);
+  hipLaunchKernelGGL((sbgemv_n_kernel<T, In, kRowsN, kUnrollN, kChainsN, kWavesN>), dim3(static_cast<unsigned>(nblocks)),
+                     dim3(kBlock), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
+                     a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, ngroups, ntasks, nblocks, part, cn.ncc, cn.cc_len);
+  if (cn.ncc > 1) {
+    const int64_t nred = (a.K * a.Nd + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL((sbgemv_n_reduce_kernel<T>), dim3(static_cast<unsigned>(nred)), dim3(kBlock), 0, s, part, a.y,
+                       a.K, a.Nd, cn.ncc, a.ldy, a.y_f32);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s) {
@@ -660,24 +739,17 @@ hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
       launch_n_narrow<double, double>(a, nvec, ns, s);
     return hipGetLastError();
   }
-  const int64_t ngroups = (a.Nd + kRowsN - 1) / kRowsN;
-  const int64_t ntasks = a.K * ngroups;
-  const int64_t nblocks = (ntasks + (kBlock / kWave) - 1) / (kBlock / kWave);
-  const dim3 grid(static_cast<unsigned>(nblocks)), block(kBlock);
-  const int64_t ldF_vec = a.ldF / nv;
-  if (compute_f32) {
-    hipLaunchKernelGGL((sbgemv_n_kernel<float, float, kRowsN, kUnrollN, kChainsN, kWavesN>), grid, block, 0, s,
-                       static_cast<const f32x4 *>(a.F), static_cast<const cx<float> *>(a.x), a.y, a.Nd, ldF_vec,
-                       nvec, a.ldx, a.ldy, a.y_f32, ngroups, ntasks, nblocks);
-  } else if (a.x_f32) {
-    hipLaunchKernelGGL((sbgemv_n_kernel<double, float, kRowsN, kUnrollN, kChainsN, kWavesN>), grid, block, 0, s,
-                       static_cast<const f64x2 *>(a.F), static_cast<const cx<float> *>(a.x), a.y, a.Nd, ldF_vec,
-                       nvec, a.ldx, a.ldy, a.y_f32, ngroups, ntasks, nblocks);
-  } else {
-    hipLaunchKernelGGL((sbgemv_n_kernel<double, double, kRowsN, kUnrollN, kChainsN, kWavesN>), grid, block, 0, s,
-                       static_cast<const f64x2 *>(a.F), static_cast<const cx<double> *>(a.x), a.y, a.Nd, ldF_vec,
-                       nvec, a.ldx, a.ldy, a.y_f32, ngroups, ntasks, nblocks);
+  ColN cn = col_n(a.K, a.Nd, nvec, resident_n_waves());
+  if (cn.ncc > 1 && !(a.part && a.part_bytes >= col_part_bytes(a.K, a.Nd, cn))) {
+    cn.ncc = 1;  // no workspace (callers outside an apply): whole rows
+    cn.cc_len = nvec;
   }
+  if (compute_f32)
+    launch_n_wide<float, float>(a, nvec, cn, s);
+  else if (a.x_f32)
+    launch_n_wide<double, float>(a, nvec, cn, s);
+  else
+    launch_n_wide<double, double>(a, nvec, cn, s);
   return hipGetLastError();
 }
 
@@ -704,11 +776,15 @@ hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
   return hipGetLastError();
 }
 
-size_t sbgemv_c_part_bytes(int64_t K, int64_t Nd, int64_t Nm) {
+size_t sbgemv_part_bytes(int64_t K, int64_t Nd, int64_t Nm) {
   const int64_t slots = resident_c_workgroups();
   size_t bytes = 0;
   for (int nv = 1; nv <= 2; ++nv) {
     const int64_t nvec = (Nm + nv - 1) / nv;
+    if (!narrow_split(K, Nd, nvec).G) {
+      const size_t bn = col_part_bytes(K, Nd, col_n(K, Nd, nvec, resident_n_waves()));
+      bytes = bn > bytes ? bn : bytes;
+    }
     const TallSplit ts = tall_split(K, Nd, nvec);
     size_t b = 0;
     if (ts.nseg) {
