@@ -535,7 +535,7 @@ ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots) {
 // most slots / tiles of them, at least kSegMinRows rows each); each
 // workgroup stores its segment's partial sums in the plan workspace and a
 // second kernel adds the segments in order.
-constexpr int64_t kSegMinRows = 64;
+constexpr int64_t kSegMinRows = 32;
 
 struct SegC {
   int64_t nseg = 1, seg_rows = 0;
