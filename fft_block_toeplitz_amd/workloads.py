@@ -77,8 +77,8 @@ def operator(Nm: int, Nd: int, Nt: int, seed: int = 0, out: np.ndarray | None = 
     """All blocks, F [Nt][Nd][Nm] float64.
 
     ``out`` may be any writable float64 array of that shape (e.g. pinned
-    host memory).  With ``workers`` > 1 the blocks are drawn by forked
-    processes into shared memory; the values are the same either way.
+    host memory).  With ``workers`` > 1 the blocks are drawn by that many
+    threads; the values are the same either way.
     """
     if out is None:
         out = np.empty((Nt, Nd, Nm), dtype=np.float64)
@@ -94,46 +94,21 @@ def operator(Nm: int, Nd: int, Nt: int, seed: int = 0, out: np.ndarray | None = 
 
 
 def _operator_parallel(out, Nm, Nd, Nt, seed, workers):
-    import multiprocessing as mp
-    from multiprocessing import shared_memory
+    """Blocks drawn by a pool of threads straight into ``out`` (numpy's
+    generator and the scaling release the GIL for bulk fills). Threads, not
+    processes: nothing is forked or executed, which matters when the calling
+    process has already initialised a GPU (a profiler can do that before the
+    program starts)."""
+    from concurrent.futures import ThreadPoolExecutor
 
-    nbytes = Nd * Nm * 8
-    chunk = max(1, min(64, (256 << 20) // nbytes))  # blocks per task
-    shm = shared_memory.SharedMemory(create=True, size=max(1, chunk * nbytes * workers))
-    try:
-        ctx = mp.get_context("fork")
-        k = 0
-        while k < Nt:
-            tasks = []
-            for w in range(workers):
-                k0 = k + w * chunk
-                if k0 >= Nt:
-                    break
-                tasks.append((shm.name, w * chunk, k0, min(Nt, k0 + chunk), Nm, Nd, Nt, seed))
-            with ctx.Pool(len(tasks)) as pool:
-                pool.map(_fill_shared, tasks)
-            view = np.ndarray((workers * chunk, Nd, Nm), dtype=np.float64, buffer=shm.buf)
-            for (_, slot, k0, k1, *_rest) in tasks:
-                out[k0:k1] = view[slot:slot + (k1 - k0)]
-            del view
-            k += workers * chunk
-    finally:
-        shm.close()
-        shm.unlink()
+    step = max(1, -(-Nt // (4 * workers)))
 
+    def fill(k0):
+        for k in range(k0, min(Nt, k0 + step)):
+            block(k, Nm, Nd, Nt, seed, out=out[k])
 
-def _fill_shared(task):
-    from multiprocessing import shared_memory
-
-    name, slot, k0, k1, Nm, Nd, Nt, seed = task
-    shm = shared_memory.SharedMemory(name=name)
-    try:
-        view = np.ndarray((slot + (k1 - k0), Nd, Nm), dtype=np.float64, buffer=shm.buf)
-        for k in range(k0, k1):
-            block(k, Nm, Nd, Nt, seed, out=view[slot + k - k0])
-        del view
-    finally:
-        shm.close()
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(fill, range(0, Nt, step)))
 
 
 def input_m(Nm: int, Nt: int, seed: int = 0) -> np.ndarray:

@@ -25,6 +25,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+import sys
 
 import numpy as np
 
@@ -50,6 +51,12 @@ def _load():
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        # compiling starts gcc as a child process; a process that has already
+        # initialised a GPU must not do that (build first, before the GPU)
+        torch = sys.modules.get("torch")
+        if torch is not None and torch.cuda.is_initialized():
+            raise RuntimeError("oracle/liboracle.so is missing or older than oracle.c: run "
+                               "__graft_entry__.build() (or oracle.build()) before using the GPU")
         build(force=True)
     lib = ctypes.CDLL(_LIB_PATH)
     P, I64 = ctypes.c_void_p, ctypes.c_int64
