@@ -536,6 +536,10 @@ ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots) {
 // workgroup stores its segment's partial sums in the plan workspace and a
 // second kernel adds the segments in order.
 constexpr int64_t kSegMinRows = 32;
+// A lane adds a column's rows in one FP32 chain; segments also keep that
+// chain at most kSegMaxRows long (Nm = 600, Nd = 4000, Nt = 256 in 3
+// segments of 1334 rows: F* error 7.4e-7 of the 1e-6 budget).
+constexpr int64_t kSegMaxRows = 512;
 
 struct SegC {
   int64_t nseg = 1, seg_rows = 0;
@@ -547,6 +551,8 @@ SegC seg_c(int64_t K, int64_t nchunks, int64_t Nd, int64_t slots) {
   int64_t n = slots / (K * nchunks);
   const int64_t by_rows = Nd / kSegMinRows;
   n = n < by_rows ? n : by_rows;
+  const int64_t by_chain = (Nd + kSegMaxRows - 1) / kSegMaxRows;
+  n = n > by_chain ? n : by_chain;
   if (n < 2) return sc;
   sc.seg_rows = (Nd + n - 1) / n;
   sc.nseg = (Nd + sc.seg_rows - 1) / sc.seg_rows;
