@@ -547,6 +547,11 @@ int condition_impl(fftmv_plan_s *p, int iters, double *kappa, double *smax, doub
   g1.Nm = g2.Nm = Nm;
   g1.F = g2.F = f32 ? p->fhat32 : p->fhat64;
   g1.ldF = g2.ldF = f32 ? p->ldF32 : p->ldF64;
+  // the plan's GEMV workspace (sized for this shape; the estimate is ordered
+  // with the plan's applies), so that tall or few-frequency blocks take the
+  // split forms here too
+  g1.part = g2.part = p->part;
+  g1.part_bytes = g2.part_bytes = p->part_bytes;
   g1.x = xin;
   g1.ldx = ldq;
   g1.x_f32 = f32;
