@@ -712,14 +712,33 @@ size_t col_part_bytes(int64_t K, int64_t Nd, const ColN &cn) {
   return cn.ncc > 1 ? static_cast<size_t>(K * cn.ncc * Nd) * 16 : 0;  // one complex (<= 16 bytes) per row and chunk
 }
 
+// Rows of at most kShortRowVecs vectors (above the narrow form's range): a
+// wave of the four-row layout finishes its rows in one or two steps and
+// pays its setup and reductions for little data, so waves take kShortRows
+// rows with one vector of each in flight and a single chain per row.
+// Measured (mixed, Nt = 1000): Nm = 100, Nd = 5000 855 -> 672 us; Nm = 120,
+// Nd = 4000 705 -> 601 us; Nm = 80, Nd = 5000 822 -> 575 us; with rows of
+// 150 or 250 vectors it is slower (799 against 717 us, 651 against 604).
+constexpr int64_t kShortRowVecs = 128;
+constexpr int kShortRows = 16;
+
 template <typename T, typename In>
 void launch_n_wide(const SbgemvArgs &a, int64_t nvec, const ColN &cn, hipStream_t s) {
   using V = typename Vec16<T>::type;
   const int nv = Vec16<T>::n;
+  cx<T> *part = static_cast<cx<T> *>(a.part);
+  if (nvec <= kShortRowVecs && cn.ncc == 1) {
+    const int64_t ngroups = (a.Nd + kShortRows - 1) / kShortRows;
+    const int64_t ntasks = a.K * ngroups;
+    const int64_t nblocks = (ntasks + (kBlock / kWave) - 1) / (kBlock / kWave);
+    hipLaunchKernelGGL((sbgemv_n_kernel<T, In, kShortRows, 1, 1, kWavesN>), dim3(static_cast<unsigned>(nblocks)),
+                       dim3(kBlock), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
+                       a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, ngroups, ntasks, nblocks, part, int64_t(1), nvec);
+    return;
+  }
   const int64_t ngroups = (a.Nd + kRowsN - 1) / kRowsN;
   const int64_t ntasks = a.K * ngroups * cn.ncc;
   const int64_t nblocks = (ntasks + (kBlock / kWave) - 1) / (kBlock / kWave);
-  cx<T> *part = static_cast<cx<T> *>(a.part);
   hipLaunchKernelGGL((sbgemv_n_kernel<T, In, kRowsN, kUnrollN, kChainsN, kWavesN>), dim3(static_cast<unsigned>(nblocks)),
                      dim3(kBlock), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
                      a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, ngroups, ntasks, nblocks, part, cn.ncc, cn.cc_len);

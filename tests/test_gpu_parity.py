@@ -98,6 +98,7 @@ SHAPES = [
     (256, 64, 16),   # 128 column vectors in FP32: the widest tall-block case
     (600, 1000, 64), # few frequencies, many rows: the short-wide F* kernel in row segments
     (20000, 4, 16),  # few frequencies, few long rows: the F kernel in column chunks
+    (150, 70, 40),   # rows of 38 / 75 vectors: the F kernel with 16 rows per wave
     (513, 2, 2000),  # wide batch at the Scale share's length, one channel in the last tile
     (33, 7, 2000),   # the Scale share's time length, narrow batches
     (3, 2, 4096),    # the longest supported transform, 2Nt = 2^13
