@@ -48,7 +48,7 @@ __global__ __launch_bounds__(TPB) void rfft_forward_ct(FwdFftArgs a, const cx<T>
   ct_passes<T, L, C, TPB, 1, g.npass, -1>(lds, tw);
 
   // split into the Nt + 1 bins; two adjacent channels per thread so that the
-  // complex64 spectrum leaves as 16-byte non-temporal stores
+  // complex64 spectrum leaves as 16-byte stores
   constexpr int NC = C > 1 ? 2 : 1;
   constexpr int CP = C / NC;
   const int c0 = (threadIdx.x % CP) * NC;
@@ -106,10 +106,15 @@ __global__ __launch_bounds__(TPB) void rfft_forward_ct(FwdFftArgs a, const cx<T>
   }
 }
 
+// Spectrum stores: non-temporal for tiles of several channels (whole 64-byte
+// runs per bin); plain for one channel per workgroup, whose 8- or 16-byte
+// bins share each cache line with the bins of neighbouring workgroups, so
+// the partial lines merge in L2 instead of reaching HBM one by one
+// (measured, 100 FP64 channels at Nt = 1000: 5.8 against 6.7 us).
 template <typename T, int L, bool ROUND, typename Src, int C, int TPB = kBlock>
 void launch_fwd_ct(const FwdFftArgs &a, const void *tw, hipStream_t s) {
   const int64_t nblocks = (a.nchan + C - 1) / C;
-  hipLaunchKernelGGL((rfft_forward_ct<T, L, C, TPB, true, ROUND, false, Src>), dim3(static_cast<unsigned>(nblocks)),
+  hipLaunchKernelGGL((rfft_forward_ct<T, L, C, TPB, (C > 1), ROUND, false, Src>), dim3(static_cast<unsigned>(nblocks)),
                      dim3(TPB), 0, s, a, static_cast<const cx<T> *>(tw), nblocks);
 }
 

@@ -276,18 +276,27 @@ __global__ __launch_bounds__(TPB) void rfft_forward_kernel(FftGeom g, FwdFftArgs
       cx<T> o = mk(dd.im * T(0.5), -dd.re * T(0.5));  // (za - zb) / 2i
       x[e] = ev + cmul(o, w);
     }
-    // non-temporal: the spectrum is consumed by the next kernel, not by this
-    // one; streaming it out keeps it from lingering dirty in the caches
+    // non-temporal when the tile holds several channels: the spectrum is
+    // consumed by the next kernel, not by this one, and streaming it out
+    // keeps it from lingering dirty in the caches. One channel per
+    // workgroup stores plainly: its bins share each cache line with those of
+    // neighbouring workgroups, and the partial lines merge in L2.
     if (d64a) {
-      store_stream(d64a + k * a.fstride64, cvt<double>(x[0]));
-      if (two) store_stream(d64b + k * a.fstride64, cvt<double>(x[1]));
+      if (C > 1) {
+        store_stream(d64a + k * a.fstride64, cvt<double>(x[0]));
+        if (two) store_stream(d64b + k * a.fstride64, cvt<double>(x[1]));
+      } else {
+        d64a[k * a.fstride64] = cvt<double>(x[0]);
+      }
     }
     if (d32a) {
       if (pack32) {
         store_stream2(d32a + k * a.fstride32, cvt<float>(x[0]), cvt<float>(x[1]));
-      } else {
+      } else if (C > 1) {
         store_stream(d32a + k * a.fstride32, cvt<float>(x[0]));
         if (two) store_stream(d32b + k * a.fstride32, cvt<float>(x[1]));
+      } else {
+        d32a[k * a.fstride32] = cvt<float>(x[0]);
       }
     }
   }
