@@ -190,6 +190,10 @@ constexpr CtTile ct_wider_fwd_tile(int L) {
 }
 constexpr int64_t kWiderBatch = 2048;
 constexpr bool has_ct(int L) { return L == 1000 || L == 2000; }
+// Work-items per channel of the widest-threaded tile above (4 channels in
+// 1024 threads; one channel in 256): a batch whose grid fits at this rate
+// fits with every tile; larger batches take the generic kernels.
+constexpr int64_t kCtItemsPerChannel = 256;
 // Channels from which the wide tile pays. Measured at Nt = 1000, forward
 // and inverse, FP32 and FP64: one channel per workgroup wins below ~256
 // channels (6.7 against 7.0 us) and collapses beyond ~1000, where its

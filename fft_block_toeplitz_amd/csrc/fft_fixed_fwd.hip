@@ -174,7 +174,7 @@ void launch_fwd_ct_any(const FwdFftArgs &a, bool compute_f32, const void *tw, hi
 // output row per frequency, byte offsets below 4 GiB
 bool fwd_ct_applies(const FftGeom &g, const FwdFftArgs &a) {
   return has_ct(g.L) && a.Nt == g.L && !(a.src_f32 && a.round_f32) && a.cpr >= a.nchan &&
-         fits_32bit(a.Nt, a.src_ld, 8) && a.nchan <= a.src_ld;
+         fits_32bit(a.Nt, a.src_ld, 8) && a.nchan <= a.src_ld && grid_fits(a.nchan, kCtItemsPerChannel);
 }
 
 }  // namespace
@@ -184,7 +184,7 @@ bool launch_fft_forward_fixed(const FftGeom &g, const FwdFftArgs &a, bool comput
   if (!fwd_ct_applies(g, a)) {
     // the frequency blocks: FP64 input and transform, any row structure and size
     const bool setup = has_ct(g.L) && a.Nt == g.L && !a.src_f32 && !a.round_f32 && !compute_f32 &&
-                       a.nchan <= a.src_ld && a.cpr >= 1 && (a.nchan + kWideBatch) / 4 < INT32_MAX;
+                       a.nchan <= a.src_ld && a.cpr >= 1 && grid_fits(a.nchan, kCtItemsPerChannel);
     if (!setup) return false;
     if (g.L == 1000)
       launch_fwd_ct_setup<1000>(a, tw, s);

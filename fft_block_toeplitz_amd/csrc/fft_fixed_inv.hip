@@ -83,7 +83,8 @@ void launch_inv_ct_any(const FftGeom &g, const InvFftArgs &a, const void *tw, hi
 
 bool inv_ct_applies(const FftGeom &g, const InvFftArgs &a) {
   return has_ct(g.L) && a.Nt == g.L && fits_32bit(g.L + 1, a.src_ld, a.src_f32 ? 8 : 16) &&
-         fits_32bit(a.Nt, a.dst_ld, 8) && a.nchan <= a.src_ld && a.nchan <= a.dst_ld;
+         fits_32bit(a.Nt, a.dst_ld, 8) && a.nchan <= a.src_ld && a.nchan <= a.dst_ld &&
+         grid_fits(a.nchan, kCtItemsPerChannel);
 }
 
 

@@ -68,7 +68,8 @@ hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool comput
   if (!blue && launch_fft_forward_fixed(g, a, compute_f32, tw, s)) return hipGetLastError();
   const FftGeom &tile = blue ? blue->gM : g;
   const FftLaunch cfg = fft_launch_config(tile, compute_f32, a.nchan);
-  if (cfg.C == 0 || (a.nchan + cfg.C - 1) / cfg.C > INT32_MAX) return hipErrorInvalidValue;
+  if (cfg.C == 0) return hipErrorInvalidValue;
+  if (!grid_fits((a.nchan + cfg.C - 1) / cfg.C, cfg.tpb)) return hipErrorInvalidConfiguration;
   if (blue) {
     const void *twM = compute_f32 ? blue->tw32 : blue->tw64, *hM = compute_f32 ? blue->hf32 : blue->hf64;
     if (!twM || !hM) return hipErrorInvalidValue;

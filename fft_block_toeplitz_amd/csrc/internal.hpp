@@ -12,6 +12,13 @@ constexpr int kBlockWide = 1024;    // threads of a wide FFT workgroup
 constexpr int kMaxLdsWide = 81920;  // LDS of a wide FFT workgroup: two fit a CU's 160 KiB
 constexpr int kMaxChannelsPerBlock = 32;
 
+// A dispatch carries its grid as a 32-bit count of work-items: a launch of
+// nblocks workgroups of tpb threads fits when nblocks * tpb < 2^32.
+// Launchers return hipErrorInvalidConfiguration for larger grids.
+inline bool grid_fits(int64_t nblocks, int64_t tpb) {
+  return nblocks >= 0 && tpb > 0 && nblocks <= static_cast<int64_t>(UINT32_MAX) / tpb;
+}
+
 // Stockham radix schedule of the length-L complex FFT that carries the
 // length-2L real FFT (even samples in the real part, odd in the imaginary).
 struct FftGeom {

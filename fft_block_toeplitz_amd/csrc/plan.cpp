@@ -72,6 +72,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow
 int status_from_hip(hipError_t e) {
   if (e == hipSuccess) return FFTMV_SUCCESS;
   if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return FFTMV_ERR_OUT_OF_MEMORY;
+  if (e == hipErrorInvalidConfiguration) return FFTMV_ERR_UNSUPPORTED_SIZE;  // a grid above 2^32 work-items
   return FFTMV_ERR_HIP;
 }
 
@@ -675,8 +676,8 @@ const char *fftmv_status_string(int status) {
     case FFTMV_SUCCESS: return "success";
     case FFTMV_ERR_INVALID_ARG: return "invalid argument";
     case FFTMV_ERR_UNSUPPORTED_SIZE:
-      return "unsupported size (Nm above 2^27, Nd above 2^31 - 1, Nt above 4096, or Nt above 2048 without a "
-             "radix-2/3/5/7 factorisation)";
+      return "unsupported size (Nm above 2^27, Nd above 2^31 - 1, Nt above 4096, Nt above 2048 without a "
+             "radix-2/3/5/7 factorisation, or a kernel grid above 2^32 work-items)";
     case FFTMV_ERR_OUT_OF_MEMORY: return "out of device memory";
     case FFTMV_ERR_HIP: return "HIP runtime error";
     case FFTMV_ERR_INTERNAL: return "internal error";

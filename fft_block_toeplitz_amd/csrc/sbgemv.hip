@@ -460,19 +460,22 @@ constexpr int kMaxVecsC = 5;  // vectors per lane, F* direction (at most)
 constexpr int kUnrollC = 2;   // rows per step (one scalar load of d_k), F* direction
 
 template <typename T, typename In, int VL>
-void launch_c(const SbgemvArgs &a, int64_t nvec, int64_t nchunks, int64_t nseg, int64_t seg_rows, hipStream_t s) {
+hipError_t launch_c(const SbgemvArgs &a, int64_t nvec, int64_t nchunks, int64_t nseg, int64_t seg_rows,
+                    hipStream_t s) {
   using V = typename Vec16<T>::type;
   const int nv = Vec16<T>::n;
   const int64_t nblocks = a.K * nchunks * nseg;
+  const int64_t nred = (a.K * nvec + kBlock - 1) / kBlock;
+  if (!grid_fits(nblocks, kBlock) || !grid_fits(nred, kBlock)) return hipErrorInvalidConfiguration;
   cx<T> *part = static_cast<cx<T> *>(a.part);
   hipLaunchKernelGGL((sbgemv_c_kernel<T, In, VL, kUnrollC>), dim3(static_cast<unsigned>(nblocks)),
                      dim3(kBlock), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
                      a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks, part, nseg, seg_rows);
   if (nseg > 1) {
-    const int64_t nred = (a.K * nvec + kBlock - 1) / kBlock;
     hipLaunchKernelGGL((sbgemv_c_reduce_kernel<T>), dim3(static_cast<unsigned>(nred)), dim3(kBlock), 0, s, part,
                        a.y, a.K, nseg, nvec, a.ldy, a.y_f32);
   }
+  return hipSuccess;
 }
 
 // Workgroups of the conjugate-transpose kernel that one CU holds at once:
@@ -564,7 +567,7 @@ size_t seg_part_bytes(int64_t K, int64_t nvec, const SegC &sc) {
 }
 
 template <typename T, typename In>
-void launch_c_vl(const SbgemvArgs &a, int64_t nvec, hipStream_t s) {
+hipError_t launch_c_vl(const SbgemvArgs &a, int64_t nvec, hipStream_t s) {
   const int64_t slots = resident_c_workgroups();
   const ChunksC c = choose_chunks_c(a.K, nvec, slots);
   SegC sc = seg_c(a.K, c.nchunks, a.Nd, slots);
@@ -573,11 +576,11 @@ void launch_c_vl(const SbgemvArgs &a, int64_t nvec, hipStream_t s) {
     sc.seg_rows = a.Nd;
   }
   switch (c.vl) {
-    case 1: launch_c<T, In, 1>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s); break;
-    case 2: launch_c<T, In, 2>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s); break;
-    case 3: launch_c<T, In, 3>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s); break;
-    case 4: launch_c<T, In, 4>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s); break;
-    default: launch_c<T, In, 5>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s); break;
+    case 1: return launch_c<T, In, 1>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+    case 2: return launch_c<T, In, 2>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+    case 3: return launch_c<T, In, 3>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+    case 4: return launch_c<T, In, 4>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+    default: return launch_c<T, In, 5>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
   }
 }
 
@@ -613,17 +616,19 @@ size_t tall_part_bytes(int64_t K, int64_t nvec, const TallSplit &ts) {
 }
 
 template <typename T, typename In>
-void launch_c_tall(const SbgemvArgs &a, int64_t nvec, const TallSplit &ts, hipStream_t s) {
+hipError_t launch_c_tall(const SbgemvArgs &a, int64_t nvec, const TallSplit &ts, hipStream_t s) {
   using V = typename Vec16<T>::type;
   const int nv = Vec16<T>::n;
   const int64_t nblocks = a.K * ts.nseg;
+  const int64_t nred = (a.K * nvec + kBlock - 1) / kBlock;
+  if (!grid_fits(nblocks, kBlock) || !grid_fits(nred, kBlock)) return hipErrorInvalidConfiguration;
   cx<T> *part = static_cast<cx<T> *>(a.part);
   hipLaunchKernelGGL((sbgemv_c_tall_kernel<T, In>), dim3(static_cast<unsigned>(nblocks)), dim3(kBlock), 0, s,
                      static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), part, a.Nd, a.ldF / nv, nvec,
                      a.ldx, ts.nseg, ts.seg_rows, nblocks);
-  const int64_t nred = (a.K * nvec + kBlock - 1) / kBlock;
   hipLaunchKernelGGL((sbgemv_c_reduce_kernel<T>), dim3(static_cast<unsigned>(nred)), dim3(kBlock), 0, s, part,
                      a.y, a.K, ts.nseg, nvec, a.ldy, a.y_f32);
+  return hipSuccess;
 }
 
 // The narrow-row form of F: rows of at most kNarrowMaxVecs vectors, in
@@ -654,24 +659,26 @@ NarrowSplit narrow_split(int64_t K, int64_t Nd, int64_t nvec) {
 }
 
 template <typename T, typename In, int G>
-void launch_n_narrow_g(const SbgemvArgs &a, int64_t nvec, const NarrowSplit &ns, hipStream_t s) {
+hipError_t launch_n_narrow_g(const SbgemvArgs &a, int64_t nvec, const NarrowSplit &ns, hipStream_t s) {
   using V = typename Vec16<T>::type;
   const int nv = Vec16<T>::n;
   const int64_t nblocks = a.K * ns.nseg;
+  if (!grid_fits(nblocks, kBlock)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((sbgemv_n_narrow_kernel<T, In, G>), dim3(static_cast<unsigned>(nblocks)), dim3(kBlock), 0, s,
                      static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd, a.ldF / nv, nvec,
                      a.ldx, a.ldy, a.y_f32, ns.nseg, ns.seg_rows, nblocks);
+  return hipSuccess;
 }
 
 template <typename T, typename In>
-void launch_n_narrow(const SbgemvArgs &a, int64_t nvec, const NarrowSplit &ns, hipStream_t s) {
+hipError_t launch_n_narrow(const SbgemvArgs &a, int64_t nvec, const NarrowSplit &ns, hipStream_t s) {
   switch (ns.G) {
-    case 1: launch_n_narrow_g<T, In, 1>(a, nvec, ns, s); break;
-    case 2: launch_n_narrow_g<T, In, 2>(a, nvec, ns, s); break;
-    case 4: launch_n_narrow_g<T, In, 4>(a, nvec, ns, s); break;
-    case 8: launch_n_narrow_g<T, In, 8>(a, nvec, ns, s); break;
-    case 16: launch_n_narrow_g<T, In, 16>(a, nvec, ns, s); break;
-    default: launch_n_narrow_g<T, In, 32>(a, nvec, ns, s); break;
+    case 1: return launch_n_narrow_g<T, In, 1>(a, nvec, ns, s);
+    case 2: return launch_n_narrow_g<T, In, 2>(a, nvec, ns, s);
+    case 4: return launch_n_narrow_g<T, In, 4>(a, nvec, ns, s);
+    case 8: return launch_n_narrow_g<T, In, 8>(a, nvec, ns, s);
+    case 16: return launch_n_narrow_g<T, In, 16>(a, nvec, ns, s);
+    default: return launch_n_narrow_g<T, In, 32>(a, nvec, ns, s);
   }
 }
 
@@ -723,7 +730,7 @@ constexpr int64_t kShortRowVecs = 128;
 constexpr int kShortRows = 16;
 
 template <typename T, typename In>
-void launch_n_wide(const SbgemvArgs &a, int64_t nvec, const ColN &cn, hipStream_t s) {
+hipError_t launch_n_wide(const SbgemvArgs &a, int64_t nvec, const ColN &cn, hipStream_t s) {
   using V = typename Vec16<T>::type;
   const int nv = Vec16<T>::n;
   cx<T> *part = static_cast<cx<T> *>(a.part);
@@ -731,22 +738,25 @@ void launch_n_wide(const SbgemvArgs &a, int64_t nvec, const ColN &cn, hipStream_
     const int64_t ngroups = (a.Nd + kShortRows - 1) / kShortRows;
     const int64_t ntasks = a.K * ngroups;
     const int64_t nblocks = (ntasks + (kBlock / kWave) - 1) / (kBlock / kWave);
+    if (!grid_fits(nblocks, kBlock)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((sbgemv_n_kernel<T, In, kShortRows, 1, 1, kWavesN>), dim3(static_cast<unsigned>(nblocks)),
                        dim3(kBlock), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
                        a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, ngroups, ntasks, nblocks, part, int64_t(1), nvec);
-    return;
+    return hipSuccess;
   }
   const int64_t ngroups = (a.Nd + kRowsN - 1) / kRowsN;
   const int64_t ntasks = a.K * ngroups * cn.ncc;
   const int64_t nblocks = (ntasks + (kBlock / kWave) - 1) / (kBlock / kWave);
+  const int64_t nred = (a.K * a.Nd + kBlock - 1) / kBlock;
+  if (!grid_fits(nblocks, kBlock) || !grid_fits(nred, kBlock)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((sbgemv_n_kernel<T, In, kRowsN, kUnrollN, kChainsN, kWavesN>), dim3(static_cast<unsigned>(nblocks)),
                      dim3(kBlock), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
                      a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, ngroups, ntasks, nblocks, part, cn.ncc, cn.cc_len);
   if (cn.ncc > 1) {
-    const int64_t nred = (a.K * a.Nd + kBlock - 1) / kBlock;
     hipLaunchKernelGGL((sbgemv_n_reduce_kernel<T>), dim3(static_cast<unsigned>(nred)), dim3(kBlock), 0, s, part, a.y,
                        a.K, a.Nd, cn.ncc, a.ldy, a.y_f32);
   }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -755,14 +765,15 @@ hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
   const int nv = compute_f32 ? 2 : 1;
   const int64_t nvec = (a.Nm + nv - 1) / nv;
   const NarrowSplit ns = narrow_split(a.K, a.Nd, nvec);
+  hipError_t e;
   if (ns.G) {
     if (compute_f32)
-      launch_n_narrow<float, float>(a, nvec, ns, s);
+      e = launch_n_narrow<float, float>(a, nvec, ns, s);
     else if (a.x_f32)
-      launch_n_narrow<double, float>(a, nvec, ns, s);
+      e = launch_n_narrow<double, float>(a, nvec, ns, s);
     else
-      launch_n_narrow<double, double>(a, nvec, ns, s);
-    return hipGetLastError();
+      e = launch_n_narrow<double, double>(a, nvec, ns, s);
+    return e != hipSuccess ? e : hipGetLastError();
   }
   ColN cn = col_n(a.K, a.Nd, nvec, resident_n_waves());
   if (cn.ncc > 1 && !(a.part && a.part_bytes >= col_part_bytes(a.K, a.Nd, cn))) {
@@ -770,12 +781,12 @@ hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
     cn.cc_len = nvec;
   }
   if (compute_f32)
-    launch_n_wide<float, float>(a, nvec, cn, s);
+    e = launch_n_wide<float, float>(a, nvec, cn, s);
   else if (a.x_f32)
-    launch_n_wide<double, float>(a, nvec, cn, s);
+    e = launch_n_wide<double, float>(a, nvec, cn, s);
   else
-    launch_n_wide<double, double>(a, nvec, cn, s);
-  return hipGetLastError();
+    e = launch_n_wide<double, double>(a, nvec, cn, s);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s) {
@@ -783,22 +794,23 @@ hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
   const int64_t nvec = (a.Nm + nv - 1) / nv;
   const TallSplit ts = tall_split(a.K, a.Nd, nvec);
   const size_t need = ts.nseg ? tall_part_bytes(a.K, nvec, ts) : 0;
+  hipError_t e;
   if (need && a.part && a.part_bytes >= need) {
     if (compute_f32)
-      launch_c_tall<float, float>(a, nvec, ts, s);
+      e = launch_c_tall<float, float>(a, nvec, ts, s);
     else if (a.x_f32)
-      launch_c_tall<double, float>(a, nvec, ts, s);
+      e = launch_c_tall<double, float>(a, nvec, ts, s);
     else
-      launch_c_tall<double, double>(a, nvec, ts, s);
-    return hipGetLastError();
+      e = launch_c_tall<double, double>(a, nvec, ts, s);
+    return e != hipSuccess ? e : hipGetLastError();
   }
   if (compute_f32)
-    launch_c_vl<float, float>(a, nvec, s);
+    e = launch_c_vl<float, float>(a, nvec, s);
   else if (a.x_f32)
-    launch_c_vl<double, float>(a, nvec, s);
+    e = launch_c_vl<double, float>(a, nvec, s);
   else
-    launch_c_vl<double, double>(a, nvec, s);
-  return hipGetLastError();
+    e = launch_c_vl<double, double>(a, nvec, s);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 size_t sbgemv_part_bytes(int64_t K, int64_t Nd, int64_t Nm) {

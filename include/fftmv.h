@@ -34,7 +34,11 @@
  *   - any other Nt <= 2048 runs in Bluestein (chirp-z) form: the length-Nt
  *     transform as a circular convolution of a power-of-two length
  *     M >= 2 Nt - 1;
- * any other size returns FFTMV_ERR_UNSUPPORTED_SIZE.
+ * any other size returns FFTMV_ERR_UNSUPPORTED_SIZE. So does a launch whose
+ * grid would exceed the 2^32 work-items of one dispatch, which only the
+ * largest batches near the memory limit reach (e.g. the setup transform of
+ * more than ~4 million channels at Nt = 4096); setup reports it for the
+ * transforms, an apply for its GEMV kernels.
  *
  * Ownership and concurrency:
  *   - fftmv_setup is synchronous: when it returns the frequency blocks are
@@ -76,7 +80,7 @@ extern "C" {
 /* ----------------------------------------------------------------- status */
 #define FFTMV_SUCCESS 0
 #define FFTMV_ERR_INVALID_ARG (-1)      /* null pointer, bad size/mask/stage  */
-#define FFTMV_ERR_UNSUPPORTED_SIZE (-2) /* Nt outside the supported lengths    */
+#define FFTMV_ERR_UNSUPPORTED_SIZE (-2) /* size outside the supported range   */
 #define FFTMV_ERR_OUT_OF_MEMORY (-3)    /* device allocation failed           */
 #define FFTMV_ERR_HIP (-4)              /* a HIP runtime call or launch failed */
 #define FFTMV_ERR_INTERNAL (-5)         /* unexpected library condition       */
