@@ -282,22 +282,24 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_narrow_kernel(const typename 
 
 // ------------------------------------------------------------------ F*
 // w_k[c] = sum_r conj(Fhat_k[r][c]) d_k[r].
-// One workgroup per (frequency k, chunk of VL*256 consecutive 16-byte column
-// vectors): each lane owns VL vectors 256 apart (a vector is two complex64
-// columns or one complex128 column) and walks down all Nd rows, one row at a
-// time, keeping one partial sum per column: no cross-lane reduction. That
-// fits a lane in 64 VGPRs, so eight waves run per SIMD and every workgroup
-// of the Main shape (2 chunks x 1001 frequencies = 2002 workgroups on 2048
-// slots) is resident at once. Each wave keeps ONE 16-byte load in flight
-// and waits for it before the next. Measured at Main: that (600 us, with
+// One workgroup of TPB threads per (frequency k, chunk of VL*TPB consecutive
+// 16-byte column vectors): each lane owns VL vectors TPB apart (a vector is
+// two complex64 columns or one complex128 column) and walks down all Nd
+// rows, one row at a time, keeping one partial sum per column: no
+// cross-lane reduction. That fits a lane in 64 VGPRs, so eight waves run
+// per SIMD and every workgroup of the Main shape (one 512-thread chunk per
+// frequency: 1001 workgroups on 1024 slots) is resident at once. Each wave
+// keeps ONE 16-byte load in flight and waits for it before the next.
+// Measured at Main with two 256-thread chunks per frequency: that (600 us, with
 // the loads through a row buffer descriptor; 604 us with 64-bit addresses,
 // which spill at 64 VGPRs) beats all VL loads of a row in flight (650 us),
 // two rows per load group at four waves per SIMD (622 us), two partial sums
 // per column (641 us, spills) and the rows split over two half-workgroups
 // (630 us). d_k[r] is the same for the whole workgroup (a scalar load, U
-// rows per load).
-template <typename T, typename In, int VL, int U>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void sbgemv_c_kernel(
+// rows per load). TPB is 256, or 512 for rows that one 512-thread tile
+// covers whole (see choose_chunks_c).
+template <typename T, typename In, int VL, int U, int TPB>
+__global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) void sbgemv_c_kernel(
     const typename Vec16<T>::type *__restrict__ F, const cx<In> *__restrict__ x, void *__restrict__ y, int64_t Nd,
     int64_t ldF_vec, int64_t nvec, int64_t ldx, int64_t ldy, bool y_f32, int64_t nchunks, int64_t nblocks,
     cx<T> *__restrict__ part, int64_t nseg, int64_t seg_rows) {
@@ -307,14 +309,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
   // tile (k, chunk), then its row segment (nseg == 1: all Nd rows, into y)
   const int64_t tile = nseg == 1 ? blk : blk / nseg, seg = blk - tile * nseg;
   const int64_t k = tile / nchunks;
-  const int64_t j0 = (tile - k * nchunks) * (kBlock * VL) + threadIdx.x;
+  const int64_t j0 = (tile - k * nchunks) * (TPB * VL) + threadIdx.x;
   const int64_t r_end = (seg + 1) * seg_rows < Nd ? (seg + 1) * seg_rows : Nd;
   const V *base = F + k * Nd * ldF_vec;
   const cx<In> *xk = x + k * ldx;
   uint32_t off[VL];  // byte offsets within a row (rows are far below 4 GiB)
 #pragma unroll
   for (int v = 0; v < VL; ++v) {
-    int64_t j = j0 + v * kBlock;
+    int64_t j = j0 + v * TPB;
     j = j < nvec ? j : nvec - 1;  // lanes past the end re-read the last vector, never store
     off[v] = static_cast<uint32_t>(j) * static_cast<uint32_t>(sizeof(V));
   }
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
 
 #pragma unroll
   for (int v = 0; v < VL; ++v) {
-    const int64_t j = j0 + v * kBlock;
+    const int64_t j = j0 + v * TPB;
     if (j < nvec) {
       cx<T> out[NV];
 #pragma unroll
@@ -459,17 +461,17 @@ constexpr int kWavesN = 4;   // waves per SIMD the registers are sized for, F di
 constexpr int kMaxVecsC = 5;  // vectors per lane, F* direction (at most)
 constexpr int kUnrollC = 2;   // rows per step (one scalar load of d_k), F* direction
 
-template <typename T, typename In, int VL>
+template <typename T, typename In, int VL, int TPB>
 hipError_t launch_c(const SbgemvArgs &a, int64_t nvec, int64_t nchunks, int64_t nseg, int64_t seg_rows,
                     hipStream_t s) {
   using V = typename Vec16<T>::type;
   const int nv = Vec16<T>::n;
   const int64_t nblocks = a.K * nchunks * nseg;
   const int64_t nred = (a.K * nvec + kBlock - 1) / kBlock;
-  if (!grid_fits(nblocks, kBlock) || !grid_fits(nred, kBlock)) return hipErrorInvalidConfiguration;
+  if (!grid_fits(nblocks, TPB) || !grid_fits(nred, kBlock)) return hipErrorInvalidConfiguration;
   cx<T> *part = static_cast<cx<T> *>(a.part);
-  hipLaunchKernelGGL((sbgemv_c_kernel<T, In, VL, kUnrollC>), dim3(static_cast<unsigned>(nblocks)),
-                     dim3(kBlock), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
+  hipLaunchKernelGGL((sbgemv_c_kernel<T, In, VL, kUnrollC, TPB>), dim3(static_cast<unsigned>(nblocks)),
+                     dim3(TPB), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
                      a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks, part, nseg, seg_rows);
   if (nseg > 1) {
     hipLaunchKernelGGL((sbgemv_c_reduce_kernel<T>), dim3(static_cast<unsigned>(nred)), dim3(kBlock), 0, s, part,
@@ -500,7 +502,11 @@ int resident_c_workgroups() {
 
 struct ChunksC {
   int64_t vl = 1, nchunks = 1;
+  int tpb = kBlock;  // threads per workgroup
 };
+
+// Workgroup of the whole-row form (see choose_chunks_c).
+constexpr int kBlockRowC = 512;
 
 // Column chunks of one frequency for the conjugate-transpose kernel. A
 // workgroup holds its chunk for all Nd rows with one load in flight per
@@ -513,6 +519,13 @@ struct ChunksC {
 // fill of the rounds, workgroups / (rounds x slots), and keeps the widest
 // chunk unless a narrower one fills clearly better: the Main and Scale
 // shapes keep 5 vectors per lane (fill 0.978 and 0.977).
+// Rows that 256 threads cannot cover at 5 vectors per lane but 512 can
+// (1281 to 2560 vectors) go whole to one 512-thread workgroup when that
+// fills the rounds as well (half as many workgroups, half as many slots):
+// each workgroup then streams its frequency block front to back. Measured
+// at Main on one box: 619 -> 606 us; with two or more 512-thread chunks per
+// row (Nm = 10000, and the Scale share) no faster than the 256-thread form,
+// which those rows keep.
 ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots) {
   ChunksC best;
   double best_fill = -1.0;
@@ -524,9 +537,15 @@ ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots) {
     const int64_t rounds = (n + slots - 1) / slots;
     const double fill = static_cast<double>(n) / static_cast<double>(rounds * slots);
     if (fill > best_fill + kFillMargin) {
-      best = {vl, nch};
+      best = {vl, nch, kBlock};
       best_fill = fill;
     }
+  }
+  if (nvec > int64_t(kBlock) * kMaxVecsC && nvec <= int64_t(kBlockRowC) * kMaxVecsC) {
+    const int64_t s2 = slots * kBlock / kBlockRowC;
+    const int64_t rounds = (K + s2 - 1) / s2;
+    const double fill = static_cast<double>(K) / static_cast<double>(rounds * s2);
+    if (fill + 1e-9 >= best_fill) best = {(nvec + kBlockRowC - 1) / kBlockRowC, 1, kBlockRowC};
   }
   return best;
 }
@@ -548,10 +567,12 @@ struct SegC {
   int64_t nseg = 1, seg_rows = 0;
 };
 
-SegC seg_c(int64_t K, int64_t nchunks, int64_t Nd, int64_t slots) {
+// slots: resident 256-thread workgroups; a chunking of c.tpb threads has
+// slots * 256 / c.tpb of them.
+SegC seg_c(int64_t K, const ChunksC &c, int64_t Nd, int64_t slots) {
   SegC sc;
   sc.seg_rows = Nd;
-  int64_t n = slots / (K * nchunks);
+  int64_t n = slots * kBlock / c.tpb / (K * c.nchunks);
   const int64_t by_rows = Nd / kSegMinRows;
   n = n < by_rows ? n : by_rows;
   const int64_t by_chain = (Nd + kSegMaxRows - 1) / kSegMaxRows;
@@ -570,17 +591,24 @@ template <typename T, typename In>
 hipError_t launch_c_vl(const SbgemvArgs &a, int64_t nvec, hipStream_t s) {
   const int64_t slots = resident_c_workgroups();
   const ChunksC c = choose_chunks_c(a.K, nvec, slots);
-  SegC sc = seg_c(a.K, c.nchunks, a.Nd, slots);
+  SegC sc = seg_c(a.K, c, a.Nd, slots);
   if (sc.nseg > 1 && !(a.part && a.part_bytes >= seg_part_bytes(a.K, nvec, sc))) {
     sc.nseg = 1;  // no workspace (callers outside an apply): all rows in one pass
     sc.seg_rows = a.Nd;
   }
+  if (c.tpb == kBlockRowC) {
+    switch (c.vl) {  // 1281..2560 vectors: 3 to 5 per lane
+      case 3: return launch_c<T, In, 3, kBlockRowC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+      case 4: return launch_c<T, In, 4, kBlockRowC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+      default: return launch_c<T, In, 5, kBlockRowC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+    }
+  }
   switch (c.vl) {
-    case 1: return launch_c<T, In, 1>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-    case 2: return launch_c<T, In, 2>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-    case 3: return launch_c<T, In, 3>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-    case 4: return launch_c<T, In, 4>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-    default: return launch_c<T, In, 5>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+    case 1: return launch_c<T, In, 1, kBlock>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+    case 2: return launch_c<T, In, 2, kBlock>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+    case 3: return launch_c<T, In, 3, kBlock>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+    case 4: return launch_c<T, In, 4, kBlock>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+    default: return launch_c<T, In, 5, kBlock>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
   }
 }
 
@@ -828,7 +856,7 @@ size_t sbgemv_part_bytes(int64_t K, int64_t Nd, int64_t Nm) {
       b = tall_part_bytes(K, nvec, ts);
     } else {
       const ChunksC c = choose_chunks_c(K, nvec, slots);
-      b = seg_part_bytes(K, nvec, seg_c(K, c.nchunks, Nd, slots));
+      b = seg_part_bytes(K, nvec, seg_c(K, c, Nd, slots));
     }
     bytes = b > bytes ? b : bytes;
   }

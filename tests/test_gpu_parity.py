@@ -99,6 +99,10 @@ SHAPES = [
     (600, 1000, 64), # few frequencies, many rows: the short-wide F* kernel in row segments
     (20000, 4, 16),  # few frequencies, few long rows: the F kernel in column chunks
     (150, 70, 40),   # rows of 38 / 75 vectors: the F kernel with 16 rows per wave
+    (3000, 300, 16), # F* rows of 1500 vectors: whole rows in 512-thread workgroups (3 per lane), row segments
+    (3500, 3, 1000), # ... 1750 complex64 vectors (4 per lane)
+    (2300, 3, 1000), # ... 2300 complex128 vectors (5 per lane) in FP64
+    (1800, 3, 1000), # ... 1800 complex128 vectors (4 per lane) in FP64
     (513, 2, 2000),  # wide batch at the Scale share's length, one channel in the last tile
     (33, 7, 2000),   # the Scale share's time length, narrow batches
     (3, 2, 4096),    # the longest supported transform, 2Nt = 2^13
