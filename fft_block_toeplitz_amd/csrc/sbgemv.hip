@@ -288,7 +288,8 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_narrow_kernel(const typename 
 // rows, one row at a time, keeping one partial sum per column: no
 // cross-lane reduction. That fits a lane in 64 VGPRs, so eight waves run
 // per SIMD and every workgroup of the Main shape (one 512-thread chunk per
-// frequency: 1001 workgroups on 1024 slots) is resident at once. Each wave
+// frequency: 1001 workgroups on 1024 slots) is resident at once; with the
+// offsets formed at each load, 10 vectors per lane still fit. Each wave
 // keeps ONE 16-byte load in flight and waits for it before the next.
 // Measured at Main with two 256-thread chunks per frequency: that (600 us, with
 // the loads through a row buffer descriptor; 604 us with 64-bit addresses,
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_narrow_kernel(const typename 
 // two rows per load group at four waves per SIMD (622 us), two partial sums
 // per column (641 us, spills) and the rows split over two half-workgroups
 // (630 us). d_k[r] is the same for the whole workgroup (a scalar load, U
-// rows per load). TPB is 256, or 512 for rows that one 512-thread tile
+// rows per load). TPB is 256, or 512 / 1024 for rows that one workgroup
 // covers whole (see choose_chunks_c).
 template <typename T, typename In, int VL, int U, int TPB>
 __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) void sbgemv_c_kernel(
@@ -313,13 +314,15 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
   const int64_t r_end = (seg + 1) * seg_rows < Nd ? (seg + 1) * seg_rows : Nd;
   const V *base = F + k * Nd * ldF_vec;
   const cx<In> *xk = x + k * ldx;
-  uint32_t off[VL];  // byte offsets within a row (rows are far below 4 GiB)
-#pragma unroll
-  for (int v = 0; v < VL; ++v) {
-    int64_t j = j0 + v * TPB;
-    j = j < nvec ? j : nvec - 1;  // lanes past the end re-read the last vector, never store
-    off[v] = static_cast<uint32_t>(j) * static_cast<uint32_t>(sizeof(V));
-  }
+  // byte offset of vector v of this lane within a row (rows are far below
+  // 4 GiB), formed at each load instead of held in VL registers; lanes past
+  // the end re-read the last vector and never store
+  const uint32_t off0 = static_cast<uint32_t>(j0) * static_cast<uint32_t>(sizeof(V));
+  const uint32_t last = static_cast<uint32_t>(nvec - 1) * static_cast<uint32_t>(sizeof(V));
+  auto off = [&](int v) {
+    const uint32_t o = off0 + static_cast<uint32_t>(v * TPB * static_cast<int>(sizeof(V)));
+    return o < last ? o : last;
+  };
 
   T ar[VL][NV], ai[VL][NV];
 #pragma unroll
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 #pragma unroll
       for (int v = 0; v < VL; ++v) {
         cx<T> f[NV];
-        split(load_stream_buf<V>(rs, off[v]), f);
+        split(load_stream_buf<V>(rs, off(v)), f);
 #pragma unroll
         for (int e = 0; e < NV; ++e) fma_conj_mul(ar[v][e], ai[v][e], f[e], d[u]);
         __builtin_amdgcn_sched_barrier(0);  // one load in flight per wave
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 #pragma unroll
     for (int v = 0; v < VL; ++v) {
       cx<T> f[NV];
-      split(load_stream_buf<V>(rs, off[v]), f);
+      split(load_stream_buf<V>(rs, off(v)), f);
 #pragma unroll
       for (int e = 0; e < NV; ++e) fma_conj_mul(ar[v][e], ai[v][e], f[e], d);
     }
@@ -505,8 +508,15 @@ struct ChunksC {
   int tpb = kBlock;  // threads per workgroup
 };
 
-// Workgroup of the whole-row form (see choose_chunks_c).
-constexpr int kBlockRowC = 512;
+// Workgroups of the whole-row form (see choose_chunks_c) and the most
+// vectors per lane it takes: 10 in FP32 (60 VGPRs), 7 in FP64, whose
+// kernels spill registers from 8 vectors per lane.
+constexpr int kBlockRowC = 512, kBlockRowWideC = 1024;
+constexpr int64_t kMaxVecsRowC = 10, kMaxVecsRowC64 = 7;
+template <typename T>
+constexpr int64_t max_vecs_row_c() {
+  return sizeof(T) == 4 ? kMaxVecsRowC : kMaxVecsRowC64;
+}
 
 // Column chunks of one frequency for the conjugate-transpose kernel. A
 // workgroup holds its chunk for all Nd rows with one load in flight per
@@ -519,14 +529,18 @@ constexpr int kBlockRowC = 512;
 // fill of the rounds, workgroups / (rounds x slots), and keeps the widest
 // chunk unless a narrower one fills clearly better: the Main and Scale
 // shapes keep 5 vectors per lane (fill 0.978 and 0.977).
-// Rows that 256 threads cannot cover at 5 vectors per lane but 512 can
-// (1281 to 2560 vectors) go whole to one 512-thread workgroup when that
-// fills the rounds as well (half as many workgroups, half as many slots):
-// each workgroup then streams its frequency block front to back. Measured
-// at Main on one box: 619 -> 606 us; with two or more 512-thread chunks per
-// row (Nm = 10000, and the Scale share) no faster than the 256-thread form,
-// which those rows keep.
-ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots) {
+// Rows that 256 threads cannot cover at 5 vectors per lane go whole to one
+// workgroup when that fills the rounds as well (fewer workgroups, as
+// fewer slots): 512 threads up to 2560 vectors (at most 5 per lane), 1024
+// threads up to 10240 (at most 10 per lane; 7168 and 7 in FP64,
+// max_row_vl). Each workgroup then streams
+// its frequency block front to back instead of sharing every row with
+// other workgroups. Measured on one box against the 256-thread chunks: Main
+// (2500 vectors, 512 x 5) 621 -> 604 us; Nm = 10000 (5000 vectors,
+// 1024 x 5) 1235 -> 1221 us; the Scale share (10000 vectors, 1024 x 10)
+// 5419 -> 5086 us. Rows cut into two or more such chunks measured no
+// faster than the 256-thread form, which longer rows keep.
+ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots, int64_t max_row_vl) {
   ChunksC best;
   double best_fill = -1.0;
   for (int64_t m = kMaxVecsC; m >= 1; --m) {
@@ -541,11 +555,12 @@ ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots) {
       best_fill = fill;
     }
   }
-  if (nvec > int64_t(kBlock) * kMaxVecsC && nvec <= int64_t(kBlockRowC) * kMaxVecsC) {
-    const int64_t s2 = slots * kBlock / kBlockRowC;
+  if (nvec > int64_t(kBlock) * kMaxVecsC && nvec <= int64_t(kBlockRowWideC) * max_row_vl) {
+    const int tpb = nvec <= int64_t(kBlockRowC) * kMaxVecsC ? kBlockRowC : kBlockRowWideC;
+    const int64_t s2 = slots * kBlock / tpb;
     const int64_t rounds = (K + s2 - 1) / s2;
     const double fill = static_cast<double>(K) / static_cast<double>(rounds * s2);
-    if (fill + 1e-9 >= best_fill) best = {(nvec + kBlockRowC - 1) / kBlockRowC, 1, kBlockRowC};
+    if (fill + 1e-9 >= best_fill) best = {(nvec + tpb - 1) / tpb, 1, tpb};
   }
   return best;
 }
@@ -590,7 +605,7 @@ size_t seg_part_bytes(int64_t K, int64_t nvec, const SegC &sc) {
 template <typename T, typename In>
 hipError_t launch_c_vl(const SbgemvArgs &a, int64_t nvec, hipStream_t s) {
   const int64_t slots = resident_c_workgroups();
-  const ChunksC c = choose_chunks_c(a.K, nvec, slots);
+  const ChunksC c = choose_chunks_c(a.K, nvec, slots, max_vecs_row_c<T>());
   SegC sc = seg_c(a.K, c, a.Nd, slots);
   if (sc.nseg > 1 && !(a.part && a.part_bytes >= seg_part_bytes(a.K, nvec, sc))) {
     sc.nseg = 1;  // no workspace (callers outside an apply): all rows in one pass
@@ -602,6 +617,24 @@ hipError_t launch_c_vl(const SbgemvArgs &a, int64_t nvec, hipStream_t s) {
       case 4: return launch_c<T, In, 4, kBlockRowC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
       default: return launch_c<T, In, 5, kBlockRowC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
     }
+  }
+  if (c.tpb == kBlockRowWideC) {
+    switch (c.vl) {  // 2561..10240 vectors: 3 to 10 per lane
+      case 3: return launch_c<T, In, 3, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+      case 4: return launch_c<T, In, 4, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+      case 5: return launch_c<T, In, 5, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+      case 6: return launch_c<T, In, 6, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+      case 7: return launch_c<T, In, 7, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+      default: break;
+    }
+    if constexpr (max_vecs_row_c<T>() == 10) {
+      switch (c.vl) {
+        case 8: return launch_c<T, In, 8, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+        case 9: return launch_c<T, In, 9, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+        default: return launch_c<T, In, 10, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+      }
+    }
+    return hipErrorInvalidValue;  // not reached: FP64 rows take at most 7 vectors per lane
   }
   switch (c.vl) {
     case 1: return launch_c<T, In, 1, kBlock>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
@@ -855,7 +888,7 @@ size_t sbgemv_part_bytes(int64_t K, int64_t Nd, int64_t Nm) {
     if (ts.nseg) {
       b = tall_part_bytes(K, nvec, ts);
     } else {
-      const ChunksC c = choose_chunks_c(K, nvec, slots);
+      const ChunksC c = choose_chunks_c(K, nvec, slots, nv == 2 ? kMaxVecsRowC : kMaxVecsRowC64);
       b = seg_part_bytes(K, nvec, seg_c(K, c, Nd, slots));
     }
     bytes = b > bytes ? b : bytes;

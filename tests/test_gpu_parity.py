@@ -103,6 +103,12 @@ SHAPES = [
     (3500, 3, 1000), # ... 1750 complex64 vectors (4 per lane)
     (2300, 3, 1000), # ... 2300 complex128 vectors (5 per lane) in FP64
     (1800, 3, 1000), # ... 1800 complex128 vectors (4 per lane) in FP64
+    (6000, 3, 1000), # whole rows in 1024-thread workgroups: 3000 complex64 (3 per lane), 6000 complex128 (6)
+    (7000, 2, 1000), # ... 3500 complex64 (4), 7000 complex128 (7, the FP64 limit)
+    (5000, 2, 1000), # ... 5000 complex128 (5)
+    (16000, 2, 1000),# ... 8000 complex64 (8)
+    (18000, 2, 1000),# ... 9000 complex64 (9)
+    (20000, 2, 1000),# ... 10000 complex64 (10, the limit); complex128 rows this long take 256-thread chunks
     (513, 2, 2000),  # wide batch at the Scale share's length, one channel in the last tile
     (33, 7, 2000),   # the Scale share's time length, narrow batches
     (3, 2, 4096),    # the longest supported transform, 2Nt = 2^13
