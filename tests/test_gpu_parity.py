@@ -109,6 +109,12 @@ SHAPES = [
     (16000, 2, 1000),# ... 8000 complex64 (8)
     (18000, 2, 1000),# ... 9000 complex64 (9)
     (20000, 2, 1000),# ... 10000 complex64 (10, the limit); complex128 rows this long take 256-thread chunks
+    (2562, 2, 1000), # form edges: 1281 complex64 vectors, the shortest whole row (512 x 3)
+    (5120, 2, 1000), # ... 2560, every lane of 512 x 5 busy; 5120 complex128 in 1024 x 5
+    (5122, 2, 1000), # ... 2561, the shortest row in 1024 threads
+    (20480, 2, 1000),# ... 10240, every lane of 1024 x 10 busy
+    (20482, 2, 1000),# ... 10241: back to 256-thread chunks
+    (5000, 1, 1000), # one row per frequency in the whole-row form
     (513, 2, 2000),  # wide batch at the Scale share's length, one channel in the last tile
     (33, 7, 2000),   # the Scale share's time length, narrow batches
     (3, 2, 4096),    # the longest supported transform, 2Nt = 2^13
