@@ -261,9 +261,7 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_narrow_kernel(const typename 
   if (live) load_x<T, In>(x + k * ldx, j, xv);
   const int64_t r1 = (seg + 1) * seg_rows < Nd ? (seg + 1) * seg_rows : Nd;
   const V *col = F + k * Nd * ldF_vec + (live ? j : 0);
-  // the G lanes of one row share q, so they run the same iterations
-#pragma unroll 4
-  for (int64_t r = seg * seg_rows + q; r < r1; r += P) {
+  auto row = [&](int64_t r) {
     T re = T(0), im = T(0);
     if (live) {
       cx<T> f[NV];
@@ -277,6 +275,16 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_narrow_kernel(const typename 
       im += __shfl_xor(im, m);
     }
     if (j == 0) store_y(y, k * ldy + r, y_f32, mk(re, im));
+  };
+  // the G lanes of one row share q, so they run the same iterations; with
+  // G > 1 the rows' cross-lane exchanges keep the compiler from unrolling a
+  // loop whose trip count is known only at run time
+  const int64_t r0 = seg * seg_rows + q;
+  if constexpr (G == 1) {
+#pragma unroll 4
+    for (int64_t r = r0; r < r1; r += P) row(r);
+  } else {
+    for (int64_t r = r0; r < r1; r += P) row(r);
   }
 }
 
