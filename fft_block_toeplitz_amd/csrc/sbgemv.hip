@@ -516,14 +516,23 @@ struct ChunksC {
   int tpb = kBlock;  // threads per workgroup
 };
 
-// Workgroups of the whole-row form (see choose_chunks_c) and the most
-// vectors per lane it takes: 10 in FP32 (60 VGPRs), 7 in FP64, whose
-// kernels spill registers from 8 vectors per lane.
-constexpr int kBlockRowC = 512, kBlockRowWideC = 1024;
-constexpr int64_t kMaxVecsRowC = 10, kMaxVecsRowC64 = 7;
+// Workgroup sizes of the whole-row form (see choose_chunks_c), each with
+// the vectors per lane it takes: at most 10 in FP32 (60 VGPRs) and 7 in
+// FP64, whose kernels spill registers from 8 vectors per lane; at least
+// enough that few lanes idle.
+struct RowFormC {
+  int tpb;
+  int64_t vl_min, vl_max32, vl_max64;
+};
+constexpr RowFormC kRowFormsC[] = {{1024, 3, 10, 7}, {512, 3, 5, 5}, {384, 4, 7, 7}};
 template <typename T>
 constexpr int64_t max_vecs_row_c() {
-  return sizeof(T) == 4 ? kMaxVecsRowC : kMaxVecsRowC64;
+  return sizeof(T) == 4 ? 10 : 7;
+}
+// resident workgroups of tpb threads, from those of 256 (eight waves per
+// SIMD either way)
+int64_t slots_for(int64_t slots256, int tpb) {
+  return slots256 / kResidentPerCuC * (int64_t(kResidentPerCuC) * kBlock / tpb);
 }
 
 // Column chunks of one frequency for the conjugate-transpose kernel. A
@@ -538,17 +547,26 @@ constexpr int64_t max_vecs_row_c() {
 // chunk unless a narrower one fills clearly better: the Main and Scale
 // shapes keep 5 vectors per lane (fill 0.978 and 0.977).
 // Rows that 256 threads cannot cover at 5 vectors per lane go whole to one
-// workgroup when that fills the rounds as well (fewer workgroups, as
-// fewer slots): 512 threads up to 2560 vectors (at most 5 per lane), 1024
-// threads up to 10240 (at most 10 per lane; 7168 and 7 in FP64,
-// max_row_vl). Each workgroup then streams
-// its frequency block front to back instead of sharing every row with
-// other workgroups. Measured on one box against the 256-thread chunks: Main
-// (2500 vectors, 512 x 5) 621 -> 604 us; Nm = 10000 (5000 vectors,
-// 1024 x 5) 1235 -> 1221 us; the Scale share (10000 vectors, 1024 x 10)
-// 5419 -> 5086 us. Rows cut into two or more such chunks measured no
-// faster than the 256-thread form, which longer rows keep.
-ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots, int64_t max_row_vl) {
+// workgroup of 1024, 512 or 384 threads (kRowFormsC; up to 10240
+// vectors, 7168 in FP64): each workgroup then streams its frequency block
+// front to back instead of sharing every row with other workgroups. Of the
+// sizes whose vectors per lane fit the row, the one that fills its rounds
+// of resident slots best is taken (on a tie, the one with fewer idle
+// lanes), and it is used unless the 256-thread chunks fill clearly better
+// (by more than kFillMargin): a row streamed whole in one round beats
+// chunks that need several. Measured on one box against the 256-thread
+// chunks: Main (2500 vectors, 512 x 5) 621 -> 604 us; 1030 frequencies of
+// 2500 vectors (Nt = 1029; 384 x 7, one round of 1280 slots where 512
+// threads would need two) 689 -> 645 us; 1200 frequencies 799 -> 734 us;
+// Nm = 10000 (5000 vectors, 1024 x 5) 1235 -> 1221 us; the Scale share
+// (10000 vectors, 1024 x 10) 5419 -> 5086 us. Rows cut into two or more
+// such chunks measured no faster than the 256-thread form, which longer
+// rows keep. A whole-row launch with a thin last round is slow (its last
+// workgroups stream whole blocks almost alone): 1401 frequencies in
+// 320-thread workgroups took 1131 us against 881 us in 256-thread chunks,
+// so 320 threads (five waves, whose workgroups did not all stay resident)
+// are not among the sizes.
+ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots, bool f32) {
   ChunksC best;
   double best_fill = -1.0;
   for (int64_t m = kMaxVecsC; m >= 1; --m) {
@@ -563,13 +581,23 @@ ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots, int64_t max_row_
       best_fill = fill;
     }
   }
-  if (nvec > int64_t(kBlock) * kMaxVecsC && nvec <= int64_t(kBlockRowWideC) * max_row_vl) {
-    const int tpb = nvec <= int64_t(kBlockRowC) * kMaxVecsC ? kBlockRowC : kBlockRowWideC;
-    const int64_t s2 = slots * kBlock / tpb;
+  if (nvec <= int64_t(kBlock) * kMaxVecsC) return best;
+  ChunksC row;
+  double row_fill = -1.0, row_busy = 0.0;
+  for (const RowFormC &f : kRowFormsC) {
+    const int64_t vl = (nvec + f.tpb - 1) / f.tpb;
+    if (vl < f.vl_min || vl > (f32 ? f.vl_max32 : f.vl_max64)) continue;
+    const int64_t s2 = slots_for(slots, f.tpb);
     const int64_t rounds = (K + s2 - 1) / s2;
     const double fill = static_cast<double>(K) / static_cast<double>(rounds * s2);
-    if (fill + 1e-9 >= best_fill) best = {(nvec + tpb - 1) / tpb, 1, tpb};
+    const double busy = static_cast<double>(nvec) / static_cast<double>(vl * f.tpb);
+    if (fill > row_fill + 1e-9 || (fill > row_fill - 1e-9 && busy > row_busy)) {
+      row = {vl, 1, f.tpb};
+      row_fill = fill;
+      row_busy = busy;
+    }
   }
+  if (row_fill >= 0 && row_fill + kFillMargin >= best_fill) best = row;
   return best;
 }
 
@@ -595,7 +623,7 @@ struct SegC {
 SegC seg_c(int64_t K, const ChunksC &c, int64_t Nd, int64_t slots) {
   SegC sc;
   sc.seg_rows = Nd;
-  int64_t n = slots * kBlock / c.tpb / (K * c.nchunks);
+  int64_t n = slots_for(slots, c.tpb) / (K * c.nchunks);
   const int64_t by_rows = Nd / kSegMinRows;
   n = n < by_rows ? n : by_rows;
   const int64_t by_chain = (Nd + kSegMaxRows - 1) / kSegMaxRows;
@@ -610,39 +638,32 @@ size_t seg_part_bytes(int64_t K, int64_t nvec, const SegC &sc) {
   return sc.nseg > 1 ? static_cast<size_t>(K * sc.nseg * nvec) * 16 : 0;
 }
 
+// the whole-row launch of c.vl vectors per lane, VL..VLMAX
+template <typename T, typename In, int TPB, int VL, int VLMAX>
+hipError_t launch_row_c(const SbgemvArgs &a, int64_t nvec, const ChunksC &c, const SegC &sc, hipStream_t s) {
+  if constexpr (VL > VLMAX) {
+    return hipErrorInvalidValue;  // not reached: choose_chunks_c keeps vl within the form's range
+  } else {
+    if (c.vl == VL) return launch_c<T, In, VL, TPB>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
+    return launch_row_c<T, In, TPB, VL + 1, VLMAX>(a, nvec, c, sc, s);
+  }
+}
+
 template <typename T, typename In>
 hipError_t launch_c_vl(const SbgemvArgs &a, int64_t nvec, hipStream_t s) {
   const int64_t slots = resident_c_workgroups();
-  const ChunksC c = choose_chunks_c(a.K, nvec, slots, max_vecs_row_c<T>());
+  const ChunksC c = choose_chunks_c(a.K, nvec, slots, sizeof(T) == 4);
   SegC sc = seg_c(a.K, c, a.Nd, slots);
   if (sc.nseg > 1 && !(a.part && a.part_bytes >= seg_part_bytes(a.K, nvec, sc))) {
     sc.nseg = 1;  // no workspace (callers outside an apply): all rows in one pass
     sc.seg_rows = a.Nd;
   }
-  if (c.tpb == kBlockRowC) {
-    switch (c.vl) {  // 1281..2560 vectors: 3 to 5 per lane
-      case 3: return launch_c<T, In, 3, kBlockRowC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-      case 4: return launch_c<T, In, 4, kBlockRowC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-      default: return launch_c<T, In, 5, kBlockRowC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-    }
-  }
-  if (c.tpb == kBlockRowWideC) {
-    switch (c.vl) {  // 2561..10240 vectors: 3 to 10 per lane
-      case 3: return launch_c<T, In, 3, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-      case 4: return launch_c<T, In, 4, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-      case 5: return launch_c<T, In, 5, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-      case 6: return launch_c<T, In, 6, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-      case 7: return launch_c<T, In, 7, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-      default: break;
-    }
-    if constexpr (max_vecs_row_c<T>() == 10) {
-      switch (c.vl) {
-        case 8: return launch_c<T, In, 8, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-        case 9: return launch_c<T, In, 9, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-        default: return launch_c<T, In, 10, kBlockRowWideC>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
-      }
-    }
-    return hipErrorInvalidValue;  // not reached: FP64 rows take at most 7 vectors per lane
+  constexpr int64_t cap = max_vecs_row_c<T>();
+  switch (c.tpb) {
+    case 1024: return launch_row_c<T, In, 1024, 3, cap>(a, nvec, c, sc, s);
+    case 512: return launch_row_c<T, In, 512, 3, 5>(a, nvec, c, sc, s);
+    case 384: return launch_row_c<T, In, 384, 4, 7>(a, nvec, c, sc, s);
+    default: break;
   }
   switch (c.vl) {
     case 1: return launch_c<T, In, 1, kBlock>(a, nvec, c.nchunks, sc.nseg, sc.seg_rows, s);
@@ -896,7 +917,7 @@ size_t sbgemv_part_bytes(int64_t K, int64_t Nd, int64_t Nm) {
     if (ts.nseg) {
       b = tall_part_bytes(K, nvec, ts);
     } else {
-      const ChunksC c = choose_chunks_c(K, nvec, slots, nv == 2 ? kMaxVecsRowC : kMaxVecsRowC64);
+      const ChunksC c = choose_chunks_c(K, nvec, slots, nv == 2);
       b = seg_part_bytes(K, nvec, seg_c(K, c, Nd, slots));
     }
     bytes = b > bytes ? b : bytes;

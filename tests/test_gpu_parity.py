@@ -115,6 +115,10 @@ SHAPES = [
     (20480, 2, 1000),# ... 10240, every lane of 1024 x 10 busy
     (20482, 2, 1000),# ... 10241: back to 256-thread chunks
     (5000, 1, 1000), # one row per frequency in the whole-row form
+    (3000, 2, 1080), # 1081 frequencies, more than 512-thread whole rows hold in one round: 384 x 4
+    (3500, 2, 1080), # ... 384 x 5
+    (4000, 2, 1080), # ... 384 x 6
+    (5000, 2, 1029), # ... 384 x 7 (1030 frequencies, radix-3/7 length)
     (513, 2, 2000),  # wide batch at the Scale share's length, one channel in the last tile
     (33, 7, 2000),   # the Scale share's time length, narrow batches
     (3, 2, 4096),    # the longest supported transform, 2Nt = 2^13
