@@ -305,8 +305,8 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_narrow_kernel(const typename 
 // two rows per load group at four waves per SIMD (622 us), two partial sums
 // per column (641 us, spills) and the rows split over two half-workgroups
 // (630 us). d_k[r] is the same for the whole workgroup (a scalar load, U
-// rows per load). TPB is 256, or 512 / 1024 for rows that one workgroup
-// covers whole (see choose_chunks_c).
+// rows per load). TPB is 256, or 384 / 512 / 1024 for rows that one
+// workgroup covers whole (see choose_chunks_c).
 template <typename T, typename In, int VL, int U, int TPB>
 __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) void sbgemv_c_kernel(
     const typename Vec16<T>::type *__restrict__ F, const cx<In> *__restrict__ x, void *__restrict__ y, int64_t Nd,
@@ -544,8 +544,9 @@ int64_t slots_for(int64_t slots256, int tpb) {
 // last round 51% full) 669 us. For each width of 5 down to 1 vectors per
 // lane (then the fewest, equal chunks that cover the row) this takes the
 // fill of the rounds, workgroups / (rounds x slots), and keeps the widest
-// chunk unless a narrower one fills clearly better: the Main and Scale
-// shapes keep 5 vectors per lane (fill 0.978 and 0.977).
+// chunk unless a narrower one fills clearly better (the Main and Scale
+// shapes would keep 5 vectors per lane, fill 0.978 and 0.977, but take the
+// whole-row form below).
 // Rows that 256 threads cannot cover at 5 vectors per lane go whole to one
 // workgroup of 1024, 512 or 384 threads (kRowFormsC; up to 10240
 // vectors, 7168 in FP64): each workgroup then streams its frequency block
