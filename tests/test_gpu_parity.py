@@ -165,6 +165,43 @@ def test_apply_matches_oracle(fm, shape, mask, staged):
     plan.close()
 
 
+def _random_cases(n=24, seed=20261202):
+    """A fixed, seeded list of block shapes (log-uniform Nm up to 12000 and Nd
+    up to 400), time lengths (radix 2/3/5/7 and Bluestein), precision masks
+    (all FP64, the page's pair, or any of the 1024) and forms (fused or five
+    kernels), within 2e7 entries of F so that the oracle stays quick: it
+    reaches combinations of the launch forms that the listed shapes do not."""
+    rng = np.random.default_rng(seed)
+    lengths = [1, 2, 3, 5, 7, 8, 12, 16, 30, 49, 64, 100, 128, 250, 256, 360, 500, 1000, 1009, 1029, 1080, 2000]
+    out = []
+    while len(out) < n:
+        Nt = int(rng.choice(lengths))
+        Nm = int(np.exp(rng.uniform(0, np.log(12000))))
+        Nd = int(np.exp(rng.uniform(0, np.log(400))))
+        if (Nt + 1) * Nd * Nm > 2e7:
+            continue
+        r = rng.random()
+        mask = 0x000 if r < 0.3 else (0x186 if r < 0.6 else int(rng.integers(0, 1024)))
+        out.append((Nm, Nd, Nt, mask, bool(rng.random() < 0.25)))
+    return out
+
+
+@pytest.mark.parametrize("rc", _random_cases(),
+                         ids=lambda rc: f"{rc[0]}x{rc[1]}x{rc[2]}-{rc[3]:#05x}" + ("-staged" if rc[4] else ""))
+def test_random_shapes_match_oracle(fm, rc):
+    Nm, Nd, Nt, mask, staged = rc
+    c = case(Nm, Nd, Nt)
+    flags = fm.FFTMV_FLAG_STAGED if staged else 0
+    note(f"random shape={(Nm, Nd, Nt)} mask={mask:#x} staged={staged}")
+    plan = fm.Plan(c.F_dev, mask | flags)
+    v = host(plan.apply(c.m_dev))
+    w = host(plan.apply_adjoint(c.d_dev))
+    ev, ew = oracle.rel_l2(v, c.v), oracle.rel_l2(w, c.w)
+    note(f"  rel err F {ev:.3e}  F* {ew:.3e}")
+    assert ev <= tol(mask, 0) and ew <= tol(mask, 1)
+    plan.close()
+
+
 @pytest.mark.parametrize("shape", [(8, 4, 16), (500, 20, 256), (37, 5, 20),
                                    (129, 65, 1000),   # wide batch, fixed-length setup kernel
                                    (37, 111, 1000),   # wide batch, odd rows: channel pairs straddle rows
