@@ -23,8 +23,8 @@ constexpr double kU64 = 1.1102230246251565e-16;  // 2^-53, binary64 unit roundof
 // configuration of the sweep); B, B_lds and t0 are a least-squares fit of
 // the measured apply times.
 constexpr double kDefaults[2][FFTMV_MODEL_PARAMS] = {
-    {0.3167, 0.1233, 0.0002667, 0.1566, 0.3162, 1, 6.9834e+12, 2.3756e+13, 3.5092e-06},  // F
-    {0.3176, 0.1239, 0.0242, 0.1557, 0.3156, 1, 6.5871e+12, 7.7313e+13, 0.0000e+00},  // F*
+    {0.3167, 0.1233, 0.0002352, 0.1566, 0.3162, 1, 6.9006e+12, 3.0736e+13, 0.0000e+00},  // F
+    {0.3176, 0.1239, 0.0242, 0.1557, 0.3156, 1, 6.5961e+12, 6.1142e+13, 0.0000e+00},  // F*
 };
 
 struct Problem {

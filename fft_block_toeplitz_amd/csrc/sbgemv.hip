@@ -235,6 +235,66 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_reduce_kernel(const cx<T> *__
   store_y(y, k * ldy + r, y_f32, acc);
 }
 
+// ------------------------------------------------------------- F, whole rows
+// v_k[r] = sum_c Fhat_k[r][c] m_k[c] with one workgroup of TPB threads per
+// frequency (FP32): lane t holds m_k's vectors t, t + TPB, ... (VL of them)
+// in registers, and the workgroup walks the rows of F̂_k one at a time, all
+// lanes reading one row together, so each workgroup streams its frequency
+// block front to back. Per row each lane adds its VL vector products in one
+// chain, each wave closes its partial with wave_sum (DPP) into LDS
+// ([Nd][waves], Nd * waves * 8 bytes), and after the last row the waves'
+// partials of each row are added in wave order: fixed orders throughout.
+template <typename In, int TPB, int VL>
+__global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) void sbgemv_n_row_kernel(
+    const f32x4 *__restrict__ F, const cx<In> *__restrict__ x, void *__restrict__ y, int64_t Nd, int64_t ldF_vec,
+    int64_t nvec, int64_t ldx, int64_t ldy, bool y_f32, int64_t nblocks) {
+  using T = float;
+  constexpr int W = TPB / kWave;
+  extern __shared__ __align__(16) unsigned char smem[];
+  cx<T> *red = reinterpret_cast<cx<T> *>(smem);
+  const int64_t k = xcd_contiguous_block(blockIdx.x, nblocks);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const f32x4 *base = F + k * Nd * ldF_vec;
+  cx<T> xv[VL][2];
+#pragma unroll
+  for (int v = 0; v < VL; ++v) {
+    const int64_t j = threadIdx.x + static_cast<int64_t>(v) * TPB;
+    if (j < nvec) {
+      load_x<T, In>(x + k * ldx, j, xv[v]);
+    } else {  // past the end: the clamped loads below add nothing
+      xv[v][0] = mk(T(0), T(0));
+      xv[v][1] = mk(T(0), T(0));
+    }
+  }
+  const uint32_t off0 = threadIdx.x * 16u, last = static_cast<uint32_t>(nvec - 1) * 16u;
+  const int64_t row_bytes = nvec * 16;
+  for (int64_t r = 0; r < Nd; ++r) {
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(base + r * ldF_vec, row_bytes);
+    T re = T(0), im = T(0);
+#pragma unroll
+    for (int v = 0; v < VL; ++v) {
+      uint32_t o = off0 + static_cast<uint32_t>(v * TPB * 16);
+      o = o < last ? o : last;
+      cx<T> f[2];
+      split(load_stream_buf<f32x4>(rs, o), f);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) fma_mul(re, im, f[e], xv[v][e]);
+      __builtin_amdgcn_sched_barrier(0);  // one load in flight per wave
+    }
+    re = wave_sum(re);
+    im = wave_sum(im);
+    if (lane == 0) red[r * W + wave] = mk(re, im);
+  }
+  __syncthreads();
+  for (int64_t r = threadIdx.x; r < Nd; r += TPB) {
+    cx<T> sum = red[r * W];
+#pragma unroll
+    for (int w = 1; w < W; ++w) sum = sum + red[r * W + w];
+    store_y(y, k * ldy + r, y_f32, sum);
+  }
+}
+
 // ----------------------------------------------------------- F, narrow rows
 // v_k[r] = sum_c Fhat_k[r][c] m_k[c] when rows have at most 32 16-byte
 // vectors: the wave-per-four-rows kernel would leave most lanes idle. Thread
@@ -850,6 +910,72 @@ hipError_t launch_n_wide(const SbgemvArgs &a, int64_t nvec, const ColN &cn, hipS
   return hipSuccess;
 }
 
+// The whole-row form of F (FP32 GEMVs): the workgroup sizes and vectors per
+// lane of the conjugate-transpose whole-row form (kRowFormsC), the one that
+// fills its rounds best, used only when that fill is at least kRowMinFillN
+// (with fewer frequencies the four-rows-per-wave kernel, whose many short
+// tasks fill any grid, stays) and the row partials fit the LDS: 64 KiB per
+// workgroup, and 160 KiB per CU for all its resident workgroups (32 waves x
+// 8 bytes per row: Nd <= 640), so that the slots counted are real.
+// Measured on one box against the four-rows-per-wave kernel: Main (2500
+// vectors, 512 x 5) 592.5 -> 588.4 us (1024 x 3: 586.7); Nm = 10000 (1024 x 5)
+// 1147 -> 1140 us; the Scale share (1024 x 10) 4610 -> 4548 us; reading two
+// rows per step, or 768-thread workgroups, measured slower.
+constexpr double kRowMinFillN = 0.9;
+constexpr int64_t kRowLdsN = 65536, kRowLdsCuN = 163840;
+
+struct RowN {
+  int tpb = 0;  // 0: not the whole-row form
+  int64_t vl = 0;
+};
+
+RowN row_n(int64_t K, int64_t Nd, int64_t nvec, int64_t slots) {
+  RowN best;
+  if (nvec <= int64_t(kBlock) * kMaxVecsC) return best;
+  double best_fill = -1.0, best_busy = 0.0;
+  for (const RowFormC &f : kRowFormsC) {
+    const int64_t vl = (nvec + f.tpb - 1) / f.tpb;
+    if (vl < f.vl_min || vl > f.vl_max32) continue;
+    const int64_t per_wg = Nd * (f.tpb / kWave) * 8;
+    if (per_wg > kRowLdsN || per_wg * (int64_t(kResidentPerCuC) * kBlock / f.tpb) > kRowLdsCuN) continue;
+    const int64_t s2 = slots_for(slots, f.tpb);
+    const int64_t rounds = (K + s2 - 1) / s2;
+    const double fill = static_cast<double>(K) / static_cast<double>(rounds * s2);
+    const double busy = static_cast<double>(nvec) / static_cast<double>(vl * f.tpb);
+    if (fill > best_fill + 1e-9 || (fill > best_fill - 1e-9 && busy > best_busy)) {
+      best = {f.tpb, vl};
+      best_fill = fill;
+      best_busy = busy;
+    }
+  }
+  if (best_fill < kRowMinFillN) best = RowN{};
+  return best;
+}
+
+template <typename In, int TPB, int VL, int VLMAX>
+hipError_t launch_n_row_vl(const SbgemvArgs &a, int64_t nvec, const RowN &rn, hipStream_t s) {
+  if constexpr (VL > VLMAX) {
+    return hipErrorInvalidValue;  // not reached: row_n keeps vl within the form's range
+  } else {
+    if (rn.vl != VL) return launch_n_row_vl<In, TPB, VL + 1, VLMAX>(a, nvec, rn, s);
+    if (!grid_fits(a.K, TPB)) return hipErrorInvalidConfiguration;
+    const size_t lds = static_cast<size_t>(a.Nd) * (TPB / kWave) * sizeof(cx<float>);
+    hipLaunchKernelGGL((sbgemv_n_row_kernel<In, TPB, VL>), dim3(static_cast<unsigned>(a.K)), dim3(TPB), lds, s,
+                       static_cast<const f32x4 *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd, a.ldF / 2, nvec,
+                       a.ldx, a.ldy, a.y_f32, a.K);
+    return hipSuccess;
+  }
+}
+
+template <typename In>
+hipError_t launch_n_row(const SbgemvArgs &a, int64_t nvec, const RowN &rn, hipStream_t s) {
+  switch (rn.tpb) {
+    case 1024: return launch_n_row_vl<In, 1024, 3, 10>(a, nvec, rn, s);
+    case 512: return launch_n_row_vl<In, 512, 3, 5>(a, nvec, rn, s);
+    default: return launch_n_row_vl<In, 384, 4, 7>(a, nvec, rn, s);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s) {
@@ -857,6 +983,13 @@ hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
   const int64_t nvec = (a.Nm + nv - 1) / nv;
   const NarrowSplit ns = narrow_split(a.K, a.Nd, nvec);
   hipError_t e;
+  if (compute_f32) {
+    const RowN rn = row_n(a.K, a.Nd, nvec, resident_c_workgroups());
+    if (rn.tpb) {
+      e = a.x_f32 ? launch_n_row<float>(a, nvec, rn, s) : launch_n_row<double>(a, nvec, rn, s);
+      return e != hipSuccess ? e : hipGetLastError();
+    }
+  }
   if (ns.G) {
     if (compute_f32)
       e = launch_n_narrow<float, float>(a, nvec, ns, s);
