@@ -269,7 +269,8 @@ def test_stage_by_stage(fm, shape, mask):
 
 @pytest.mark.parametrize("shape,staged", [((500, 20, 256), False), ((37, 5, 20), False), ((37, 5, 1000), False),
                                           ((37, 5, 63), False),
-                                          ((37, 5, 11), False), ((37, 5, 1000), True), ((4103, 3, 1000), True)])
+                                          ((37, 5, 11), False), ((37, 5, 1000), True), ((4103, 3, 1000), True),
+                                          ((4103, 3, 1000), False)])
 def test_all_precision_masks(fm, shape, staged):
     """Every one of the 32 per-stage precision choices of each direction,
     on one plan holding Fhat in both precisions (fused, or the five-kernel
