@@ -96,6 +96,15 @@ __device__ __forceinline__ void store_vec(void *y, int64_t idx, bool f32, const 
   }
 }
 
+// 16 bytes at byte_off through a row descriptor, non-temporal (aux bit 1).
+// A buffer store with the cache policy as an immediate: a plain pointer
+// store chosen by a runtime flag next to it would be merged with it, and
+// the non-temporal hint dropped.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_stream_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 w) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), r, static_cast<int>(byte_off), 0, 2);
+}
+
 template <typename T>
 __device__ __forceinline__ void store_y(void *y, int64_t idx, bool f32, cx<T> v) {
   if (f32)
@@ -366,12 +375,13 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_narrow_kernel(const typename 
 // per column (641 us, spills) and the rows split over two half-workgroups
 // (630 us). d_k[r] is the same for the whole workgroup (a scalar load, U
 // rows per load). TPB is 256, or 384 / 512 / 1024 for rows that one
-// workgroup covers whole (see choose_chunks_c).
+// workgroup covers whole (see choose_chunks_c). nt_y: FP32 w is written
+// with non-temporal stores (large outputs, see kStreamOutBytesC).
 template <typename T, typename In, int VL, int U, int TPB>
 __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) void sbgemv_c_kernel(
     const typename Vec16<T>::type *__restrict__ F, const cx<In> *__restrict__ x, void *__restrict__ y, int64_t Nd,
     int64_t ldF_vec, int64_t nvec, int64_t ldx, int64_t ldy, bool y_f32, int64_t nchunks, int64_t nblocks,
-    cx<T> *__restrict__ part, int64_t nseg, int64_t seg_rows) {
+    cx<T> *__restrict__ part, int64_t nseg, int64_t seg_rows, bool nt_y) {
   using V = typename Vec16<T>::type;
   constexpr int NV = Vec16<T>::n;
   const int64_t blk = xcd_contiguous_block(blockIdx.x, nblocks);
@@ -429,6 +439,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     }
   }
 
+  const __amdgpu_buffer_rsrc_t yrs = row_rsrc(static_cast<cx<float> *>(y) + k * ldy, nvec * 16);
 #pragma unroll
   for (int v = 0; v < VL; ++v) {
     const int64_t j = j0 + v * TPB;
@@ -437,6 +448,13 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 #pragma unroll
       for (int e = 0; e < NV; ++e) out[e] = mk(ar[v][e], ai[v][e]);
       if (nseg == 1) {
+        if constexpr (sizeof(T) == 4) {
+          if (nt_y) {  // FP32 w only (the launcher sets nt_y for no other case)
+            store_stream_buf(yrs, static_cast<uint32_t>(j) * 16u,
+                             f32x4{out[0].re, out[0].im, out[1].re, out[1].im});
+            continue;
+          }
+        }
         store_vec(y, k * ldy + j * NV, y_f32, out);
       } else {
 #pragma unroll
@@ -532,6 +550,17 @@ constexpr int kWavesN = 4;   // waves per SIMD the registers are sized for, F di
 constexpr int kMaxVecsC = 5;  // vectors per lane, F* direction (at most)
 constexpr int kUnrollC = 2;   // rows per step (one scalar load of d_k), F* direction
 
+// Output size (bytes of w over all frequencies) from which the conjugate-
+// transpose kernel stores FP32 w with non-temporal stores. Measured for FP32 w at
+// K = 2001, Nd = 100, whole-row workgroups of 1024 threads: from 128 MB of
+// output (Nm = 8000) to 320 MB (Nm = 20000) the kernel runs 5-7% faster
+// with them (4.88 against 5.22 ms at Nm = 20000); the end-of-workgroup store
+// burst through the caches otherwise costs about 10% of the kernel (4.55 ms
+// with the stores left out). At Nm = 5000, K = 1001 (40 MB) they gain
+// nothing (638 against 636 us), and an output that fits the last-level
+// cache can be read from there by the inverse FFT that follows.
+constexpr int64_t kStreamOutBytesC = int64_t(64) << 20;
+
 template <typename T, typename In, int VL, int TPB>
 hipError_t launch_c(const SbgemvArgs &a, int64_t nvec, int64_t nchunks, int64_t nseg, int64_t seg_rows,
                     hipStream_t s) {
@@ -541,9 +570,10 @@ hipError_t launch_c(const SbgemvArgs &a, int64_t nvec, int64_t nchunks, int64_t 
   const int64_t nred = (a.K * nvec + kBlock - 1) / kBlock;
   if (!grid_fits(nblocks, TPB) || !grid_fits(nred, kBlock)) return hipErrorInvalidConfiguration;
   cx<T> *part = static_cast<cx<T> *>(a.part);
+  const bool nt_y = sizeof(T) == 4 && a.y_f32 && nseg == 1 && a.K * a.ldy * 8 >= kStreamOutBytesC;
   hipLaunchKernelGGL((sbgemv_c_kernel<T, In, VL, kUnrollC, TPB>), dim3(static_cast<unsigned>(nblocks)),
                      dim3(TPB), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
-                     a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks, part, nseg, seg_rows);
+                     a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks, part, nseg, seg_rows, nt_y);
   if (nseg > 1) {
     hipLaunchKernelGGL((sbgemv_c_reduce_kernel<T>), dim3(static_cast<unsigned>(nred)), dim3(kBlock), 0, s, part,
                        a.y, a.K, nseg, nvec, a.ldy, a.y_f32);
