@@ -101,8 +101,27 @@ __device__ __forceinline__ void store_vec(void *y, int64_t idx, bool f32, const 
 // store chosen by a runtime flag next to it would be merged with it, and
 // the non-temporal hint dropped.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void store_stream_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 w) {
+template <typename W>
+__device__ __forceinline__ void store_stream_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, W w) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), r, static_cast<int>(byte_off), 0, 2);
+}
+
+// store_vec through a descriptor of row y_k with non-temporal stores; j is
+// the 16-byte input vector index. Not for FP64 sums into FP32 w (8-byte
+// stores).
+template <typename T>
+__device__ __forceinline__ void store_vec_stream(__amdgpu_buffer_rsrc_t r, int64_t j, bool f32, const cx<T> *v) {
+  const uint32_t o = static_cast<uint32_t>(j) * 16u;
+  if constexpr (sizeof(T) == 4) {
+    if (f32) {
+      store_stream_buf(r, o, f32x4{v[0].re, v[0].im, v[1].re, v[1].im});
+    } else {
+      store_stream_buf(r, 2u * o, f64x2{v[0].re, v[0].im});
+      store_stream_buf(r, 2u * o + 16u, f64x2{v[1].re, v[1].im});
+    }
+  } else {
+    store_stream_buf(r, o, f64x2{v[0].re, v[0].im});
+  }
 }
 
 template <typename T>
@@ -375,8 +394,8 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_narrow_kernel(const typename 
 // per column (641 us, spills) and the rows split over two half-workgroups
 // (630 us). d_k[r] is the same for the whole workgroup (a scalar load, U
 // rows per load). TPB is 256, or 384 / 512 / 1024 for rows that one
-// workgroup covers whole (see choose_chunks_c). nt_y: FP32 w is written
-// with non-temporal stores (large outputs, see kStreamOutBytesC).
+// workgroup covers whole (see choose_chunks_c). nt_y: w is written with
+// non-temporal stores (large outputs, see kStreamOutBytesC).
 template <typename T, typename In, int VL, int U, int TPB>
 __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) void sbgemv_c_kernel(
     const typename Vec16<T>::type *__restrict__ F, const cx<In> *__restrict__ x, void *__restrict__ y, int64_t Nd,
@@ -439,7 +458,10 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     }
   }
 
-  const __amdgpu_buffer_rsrc_t yrs = row_rsrc(static_cast<cx<float> *>(y) + k * ldy, nvec * 16);
+  // row y_k for non-temporal stores: nvec * NV complex entries
+  const __amdgpu_buffer_rsrc_t yrs =
+      y_f32 ? row_rsrc(static_cast<cx<float> *>(y) + k * ldy, nvec * NV * 8)
+            : row_rsrc(static_cast<cx<double> *>(y) + k * ldy, nvec * NV * 16);
 #pragma unroll
   for (int v = 0; v < VL; ++v) {
     const int64_t j = j0 + v * TPB;
@@ -448,14 +470,10 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 #pragma unroll
       for (int e = 0; e < NV; ++e) out[e] = mk(ar[v][e], ai[v][e]);
       if (nseg == 1) {
-        if constexpr (sizeof(T) == 4) {
-          if (nt_y) {  // FP32 w only (the launcher sets nt_y for no other case)
-            store_stream_buf(yrs, static_cast<uint32_t>(j) * 16u,
-                             f32x4{out[0].re, out[0].im, out[1].re, out[1].im});
-            continue;
-          }
-        }
-        store_vec(y, k * ldy + j * NV, y_f32, out);
+        if (nt_y)
+          store_vec_stream(yrs, j, y_f32, out);
+        else
+          store_vec(y, k * ldy + j * NV, y_f32, out);
       } else {
 #pragma unroll
         for (int e = 0; e < NV; ++e) part[((k * nseg + seg) * nvec + j) * NV + e] = out[e];
@@ -551,7 +569,8 @@ constexpr int kMaxVecsC = 5;  // vectors per lane, F* direction (at most)
 constexpr int kUnrollC = 2;   // rows per step (one scalar load of d_k), F* direction
 
 // Output size (bytes of w over all frequencies) from which the conjugate-
-// transpose kernel stores FP32 w with non-temporal stores. Measured for FP32 w at
+// transpose kernel stores w with non-temporal stores (not FP64 sums into
+// FP32 w, whose stores are 8 bytes). Measured for FP32 w at
 // K = 2001, Nd = 100, whole-row workgroups of 1024 threads: from 128 MB of
 // output (Nm = 8000) to 320 MB (Nm = 20000) the kernel runs 5-7% faster
 // with them (4.88 against 5.22 ms at Nm = 20000); the end-of-workgroup store
@@ -570,7 +589,8 @@ hipError_t launch_c(const SbgemvArgs &a, int64_t nvec, int64_t nchunks, int64_t 
   const int64_t nred = (a.K * nvec + kBlock - 1) / kBlock;
   if (!grid_fits(nblocks, TPB) || !grid_fits(nred, kBlock)) return hipErrorInvalidConfiguration;
   cx<T> *part = static_cast<cx<T> *>(a.part);
-  const bool nt_y = sizeof(T) == 4 && a.y_f32 && nseg == 1 && a.K * a.ldy * 8 >= kStreamOutBytesC;
+  const bool nt_y = nseg == 1 && !(sizeof(T) == 8 && a.y_f32) &&
+                    a.K * a.ldy * (a.y_f32 ? 8 : 16) >= kStreamOutBytesC;
   hipLaunchKernelGGL((sbgemv_c_kernel<T, In, VL, kUnrollC, TPB>), dim3(static_cast<unsigned>(nblocks)),
                      dim3(TPB), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
                      a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks, part, nseg, seg_rows, nt_y);
