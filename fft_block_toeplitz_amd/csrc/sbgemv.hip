@@ -381,8 +381,11 @@ __global__ __launch_bounds__(kBlock) void sbgemv_n_narrow_kernel(const typename 
 // One workgroup of TPB threads per (frequency k, chunk of VL*TPB consecutive
 // 16-byte column vectors): each lane owns VL vectors TPB apart (a vector is
 // two complex64 columns or one complex128 column) and walks down all Nd
-// rows, one row at a time, keeping one partial sum per column: no
-// cross-lane reduction. That fits a lane in 64 VGPRs, so eight waves run
+// rows in steps of U rows, keeping one partial sum per column: no
+// cross-lane reduction. The U products of a step are added together before
+// they enter the column's sum, so that in FP32 no chain is longer than
+// about Nd / U additions (one chain over all Nd rows costs 2.3x the error at
+// Nd = 100). That fits a lane in 64 VGPRs, so eight waves run
 // per SIMD and every workgroup of the Main shape (one 512-thread chunk per
 // frequency: 1001 workgroups on 1024 slots) is resident at once; with the
 // offsets formed at each load, 10 vectors per lane still fit. Each wave
@@ -433,16 +436,47 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     cx<T> d[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) d[u] = cvt<T>(xk[r + u]);
+    if constexpr (sizeof(T) == 4) {
+      // FP32: the U rows' products of each column are summed first and
+      // enter the column's sum once, so the chains are U and Nd / U
+      // additions long instead of one of Nd
+      __amdgpu_buffer_rsrc_t rs[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const __amdgpu_buffer_rsrc_t rs = row_rsrc(base + (r + u) * ldF_vec, row_bytes);
+      for (int u = 0; u < U; ++u) rs[u] = row_rsrc(base + (r + u) * ldF_vec, row_bytes);
 #pragma unroll
       for (int v = 0; v < VL; ++v) {
-        cx<T> f[NV];
-        split(load_stream_buf<V>(rs, off(v)), f);
+        T gr[NV], gi[NV];
 #pragma unroll
-        for (int e = 0; e < NV; ++e) fma_conj_mul(ar[v][e], ai[v][e], f[e], d[u]);
-        __builtin_amdgcn_sched_barrier(0);  // one load in flight per wave
+        for (int e = 0; e < NV; ++e) gr[e] = gi[e] = T(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          cx<T> f[NV];
+          split(load_stream_buf<V>(rs[u], off(v)), f);
+#pragma unroll
+          for (int e = 0; e < NV; ++e) fma_conj_mul(gr[e], gi[e], f[e], d[u]);
+          __builtin_amdgcn_sched_barrier(0);  // one load in flight per wave
+        }
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+          ar[v][e] += gr[e];
+          ai[v][e] += gi[e];
+        }
+      }
+    } else {
+      // FP64: rows added to the column sums one by one (the chain length
+      // is far below the FP64 error budget; the row step keeps the
+      // registers of the longest rows without spills)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(base + (r + u) * ldF_vec, row_bytes);
+#pragma unroll
+        for (int v = 0; v < VL; ++v) {
+          cx<T> f[NV];
+          split(load_stream_buf<V>(rs, off(v)), f);
+#pragma unroll
+          for (int e = 0; e < NV; ++e) fma_conj_mul(ar[v][e], ai[v][e], f[e], d[u]);
+          __builtin_amdgcn_sched_barrier(0);  // one load in flight per wave
+        }
       }
     }
   }
@@ -566,7 +600,16 @@ constexpr int kUnrollN = 2;  // vectors per row in flight, F direction
 constexpr int kChainsN = 4;  // partial sums per row and lane, F direction
 constexpr int kWavesN = 4;   // waves per SIMD the registers are sized for, F direction
 constexpr int kMaxVecsC = 5;  // vectors per lane, F* direction (at most)
-constexpr int kUnrollC = 2;   // rows per step (one scalar load of d_k), F* direction
+// Rows per step of the conjugate-transpose kernel (F* direction): one scalar
+// load of d_k per row; in FP32 the step's products of each column are
+// summed before they enter the column's sum. Measured at Nm=5000, Nd=100,
+// Nt=1000 (FP32, 512-thread whole rows): F* error of the FP32 SBGEMV alone
+// 1.94e-7 with every row added to the column sum directly, 1.07e-7 in steps
+// of 2 rows, 8.6e-8 of 4, 8.3e-8 of 5; kernel time 588, 590, 592, 592 us.
+// FP64 keeps steps of 2 (five rows of complex128 d_k spill the widest rows),
+// and so does FP32 at 8 vectors per lane (5 and 4 rows spill 2 VGPRs there).
+template <typename T, int VL>
+constexpr int unroll_c() { return sizeof(T) == 4 && VL != 8 ? 5 : 2; }
 
 // Output size (bytes of w over all frequencies) from which the conjugate-
 // transpose kernel stores w with non-temporal stores (not FP64 sums into
@@ -591,7 +634,7 @@ hipError_t launch_c(const SbgemvArgs &a, int64_t nvec, int64_t nchunks, int64_t 
   cx<T> *part = static_cast<cx<T> *>(a.part);
   const bool nt_y = nseg == 1 && !(sizeof(T) == 8 && a.y_f32) &&
                     a.K * a.ldy * (a.y_f32 ? 8 : 16) >= kStreamOutBytesC;
-  hipLaunchKernelGGL((sbgemv_c_kernel<T, In, VL, kUnrollC, TPB>), dim3(static_cast<unsigned>(nblocks)),
+  hipLaunchKernelGGL((sbgemv_c_kernel<T, In, VL, unroll_c<T, VL>(), TPB>), dim3(static_cast<unsigned>(nblocks)),
                      dim3(TPB), 0, s, static_cast<const V *>(a.F), static_cast<const cx<In> *>(a.x), a.y, a.Nd,
                      a.ldF / nv, nvec, a.ldx, a.ldy, a.y_f32, nchunks, nblocks, part, nseg, seg_rows, nt_y);
   if (nseg > 1) {
@@ -720,9 +763,10 @@ ChunksC choose_chunks_c(int64_t K, int64_t nvec, int64_t slots, bool f32) {
 // workgroup stores its segment's partial sums in the plan workspace and a
 // second kernel adds the segments in order.
 constexpr int64_t kSegMinRows = 32;
-// A lane adds a column's rows in one FP32 chain; segments also keep that
-// chain at most kSegMaxRows long (Nm = 600, Nd = 4000, Nt = 256 in 3
-// segments of 1334 rows: F* error 7.4e-7 of the 1e-6 budget).
+// Segments are also at most kSegMaxRows long, which bounds the FP32 chain
+// of a column sum to about kSegMaxRows / 5 additions in FP32 (Nm = 600, Nd = 4000,
+// Nt = 256 in 3 segments of 1334 rows, every row added to the column sum
+// directly: F* error 7.4e-7 of the 1e-6 budget).
 constexpr int64_t kSegMaxRows = 512;
 
 struct SegC {
