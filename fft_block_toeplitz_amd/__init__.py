@@ -42,7 +42,10 @@ FFTMV_FLAG_STAGED = 1 << 16
 FFTMV_FLAG_FHAT_BOTH = 1 << 17
 FFTMV_MODEL_PARAMS = 9
 
-EXPORTS = ("fftmv_setup", "fftmv_apply", "fftmv_apply_adjoint", "fftmv_destroy", "fftmv_status_string",
+FFTMV_SCRATCH_BYTES = 128 << 20
+
+EXPORTS = ("fftmv_setup", "fftmv_apply", "fftmv_apply_adjoint", "fftmv_apply_scratch", "fftmv_destroy",
+           "fftmv_status_string",
            "fftmv_query", "fftmv_set_mask", "fftmv_run_stages", "fftmv_buffer", "fftmv_model_defaults",
            "fftmv_predict", "fftmv_pareto_front", "fftmv_select_precision", "fftmv_condition", "fftmv_version")
 
@@ -85,6 +88,7 @@ def lib() -> ctypes.CDLL:
     L.fftmv_setup.argtypes = [ctypes.POINTER(P), P, I64, I64, I64, U32, P]
     L.fftmv_apply.argtypes = [P, P, P, P]
     L.fftmv_apply_adjoint.argtypes = [P, P, P, P]
+    L.fftmv_apply_scratch.argtypes = [P, I, P, P, P]
     L.fftmv_destroy.argtypes = [P]
     L.fftmv_status_string.argtypes = [I]
     L.fftmv_status_string.restype = ctypes.c_char_p
@@ -124,6 +128,10 @@ def fftmv_apply(plan: int, m_dev: int, v_dev: int, stream: int = 0) -> None:
 
 def fftmv_apply_adjoint(plan: int, d_dev: int, w_dev: int, stream: int = 0) -> None:
     _check(lib().fftmv_apply_adjoint(plan, d_dev, w_dev, stream), "fftmv_apply_adjoint")
+
+
+def fftmv_apply_scratch(plan: int, direction: int, in_dev: int, out_dev: int, stream: int = 0) -> None:
+    _check(lib().fftmv_apply_scratch(plan, direction, in_dev, out_dev, stream), "fftmv_apply_scratch")
 
 
 def fftmv_destroy(plan: int) -> None:

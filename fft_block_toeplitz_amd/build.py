@@ -12,7 +12,7 @@ LIB = os.path.join(HERE, "libfftmv.so")
 SOURCES = [os.path.join(HERE, "csrc", f)
            for f in ("fft_generic_fwd.hip", "fft_generic_inv.hip", "fft_generic_fwd_blue.hip",
                      "fft_generic_inv_blue.hip", "fft_fixed_fwd.hip", "fft_fixed_inv.hip", "sbgemv.hip",
-                     "padcast.hip", "condition.hip", "plan.cpp", "precision.cpp")]
+                     "padcast.hip", "condition.hip", "scratch.hip", "plan.cpp", "precision.cpp")]
 HEADERS = [os.path.join(ROOT, "include", "fftmv.h")] + [
     os.path.join(HERE, "csrc", f) for f in ("common.hpp", "internal.hpp", "fft_device.hpp", "fft_fixed.hpp",
                                             "fft_generic.hpp")]

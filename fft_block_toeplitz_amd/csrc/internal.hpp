@@ -177,6 +177,16 @@ hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
 size_t sbgemv_part_bytes(int64_t K, int64_t Nd, int64_t Nm);
 hipError_t launch_cast(const CastArgs &a, hipStream_t s);
 
+// The static device scratch of the allocation-free apply (scratch.hip):
+// kScratchBytes per GPU, 256-byte aligned. scratch_device_ptr returns the
+// current device's copy (its address looked up once per device).
+constexpr size_t kScratchBytes = size_t(128) << 20;
+hipError_t scratch_device_ptr(void **out);
+// Zero `bytes` bytes (a multiple of 4) at base + r * pitch_bytes + off_bytes
+// for every row r < rows, with a kernel (no memset node in a captured graph).
+hipError_t launch_zero_cols(void *base, int64_t rows, int64_t pitch_bytes, int64_t off_bytes, int64_t bytes,
+                            hipStream_t s);
+
 // Lanczos process on the per-frequency Gram matrices (condition.hip). One
 // frequency's vectors have n complex entries; vector j of frequency k is
 // Q + (j * K + k) * ldq (complex128).

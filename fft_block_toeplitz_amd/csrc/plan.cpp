@@ -315,22 +315,54 @@ bool overlap(const fftmv_plan_s *p, int dir, const double *in, const double *out
   return i0 < o1 && o0 < i1;
 }
 
+bool apply_args_ok(const fftmv_plan_s *p, int dir, const double *in, double *out) {
+  if (!p || !in || !out || !aligned8(in) || !aligned8(out)) return false;
+  return !overlap(p, dir, in, out) && on_plan_device(p);
+}
+
+// The launches of one apply (five-kernel or fused form) with p's buffers.
+hipError_t launch_apply(const fftmv_plan_s *p, int dir, const double *in, double *out, hipStream_t s) {
+  if (p->flags & FFTMV_FLAG_STAGED) return run_range(p, dir, 1, 5, in, out, s);
+  hipError_t e = stage_fft(p, dir, in, true, s);
+  if (e == hipSuccess) e = stage_sbgemv(p, dir, s);
+  if (e == hipSuccess) e = stage_ifft(p, dir, out, true, s);
+  return e;
+}
+
 int apply_dir(fftmv_plan_t p, int dir, const double *in, double *out, hipStream_t s) {
-  if (!p || !in || !out || !aligned8(in) || !aligned8(out)) return FFTMV_ERR_INVALID_ARG;
-  if (overlap(p, dir, in, out) || !on_plan_device(p)) return FFTMV_ERR_INVALID_ARG;
+  if (!apply_args_ok(p, dir, in, out)) return FFTMV_ERR_INVALID_ARG;
   try {
-    hipError_t e;
-    if (p->flags & FFTMV_FLAG_STAGED) {
-      e = run_range(p, dir, 1, 5, in, out, s);
-    } else {
-      e = stage_fft(p, dir, in, true, s);
-      if (e == hipSuccess) e = stage_sbgemv(p, dir, s);
-      if (e == hipSuccess) e = stage_ifft(p, dir, out, true, s);
-    }
-    return status_from_hip(e);
+    return status_from_hip(launch_apply(p, dir, in, out, s));
   } catch (...) {
     return FFTMV_ERR_INTERNAL;
   }
+}
+
+// Bytes of the static scratch an apply of direction dir takes, and the
+// plan's stage buffers and GEMV workspace laid out in it (each region
+// 256-byte aligned, buffers in the precision the mask gives them). Returns
+// false when they do not fit kScratchBytes.
+bool scratch_layout(const fftmv_plan_s *p, int dir, unsigned char *base, fftmv_plan_s *view, size_t *need) {
+  const bool staged = p->flags & FFTMV_FLAG_STAGED;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~size_t(255);
+    return at;
+  };
+  for (int st = staged ? 1 : 2; st <= (staged ? 4 : 3); ++st) {
+    const bool cplx = st == 2 || st == 3;
+    const int64_t rows = cplx ? p->K : p->Nt;
+    const size_t esz = (cplx ? 16 : 8) / (buf_f32(p->prec, dir, st) ? 2 : 1);
+    const size_t at = take(static_cast<size_t>(rows * p->buf[dir][st].ld) * esz);
+    if (view) view->buf[dir][st].p = base + at;
+  }
+  if (p->part_bytes) {
+    const size_t at = take(p->part_bytes);
+    if (view) view->part = base + at;
+  }
+  *need = off;
+  return off <= kScratchBytes;
 }
 
 int setup_impl(fftmv_plan_s *p, const double *F, hipStream_t s) {
@@ -657,6 +689,34 @@ int fftmv_apply(fftmv_plan_t plan, const double *m_dev, double *v_dev, hipStream
 
 int fftmv_apply_adjoint(fftmv_plan_t plan, const double *d_dev, double *w_dev, hipStream_t stream) {
   return apply_dir(plan, FFTMV_DIR_FADJ, d_dev, w_dev, stream);
+}
+
+int fftmv_apply_scratch(fftmv_plan_t plan, int dir, const double *in, double *out, hipStream_t stream) {
+  if ((dir != FFTMV_DIR_F && dir != FFTMV_DIR_FADJ) || !apply_args_ok(plan, dir, in, out))
+    return FFTMV_ERR_INVALID_ARG;
+  try {
+    size_t need = 0;
+    if (!scratch_layout(plan, dir, nullptr, nullptr, &need)) return FFTMV_ERR_UNSUPPORTED_SIZE;
+    void *base = nullptr;
+    hipError_t e = scratch_device_ptr(&base);
+    if (e != hipSuccess) return status_from_hip(e);
+    // the plan with its stage buffers and GEMV workspace in the scratch (a
+    // copy of the plan's description; nothing is allocated or freed)
+    fftmv_plan_s view = *plan;
+    scratch_layout(plan, dir, static_cast<unsigned char *>(base), &view, &need);
+    // The scratch keeps whatever the last call on this GPU left. The GEMV
+    // reads the stage-2 spectrum in 16-byte vectors, which can cover the
+    // padding entry after a row's last channel: those columns must hold
+    // zeros (a kernel clears them; no memset node under stream capture).
+    const StageBuf &b2 = view.buf[dir][2];
+    const int64_t nin = channels_in(&view, dir);
+    const int64_t esz2 = buf_f32(view.prec, dir, 2) ? 8 : 16;
+    e = launch_zero_cols(b2.p, view.K, b2.ld * esz2, nin * esz2, (b2.ld - nin) * esz2, stream);
+    if (e == hipSuccess) e = launch_apply(&view, dir, in, out, stream);
+    return status_from_hip(e);
+  } catch (...) {
+    return FFTMV_ERR_INTERNAL;
+  }
 }
 
 int fftmv_destroy(fftmv_plan_t plan) {

@@ -134,6 +134,27 @@ FFTMV_API int fftmv_apply(fftmv_plan_t plan, const double *m_dev, double *v_dev,
  * d_dev [Nt][Nd] FP64 in, w_dev [Nt][Nm] FP64 out; asynchronous. */
 FFTMV_API int fftmv_apply_adjoint(fftmv_plan_t plan, const double *d_dev, double *w_dev, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under stream
+ * capture, serving loops, harnesses that forbid allocation): an apply of
+ * direction dir (FFTMV_DIR_F: v = F m, as fftmv_apply; FFTMV_DIR_FADJ:
+ * w = F* d, as fftmv_apply_adjoint) with the same kernels and the same
+ * results, whose intermediate spectra and partial sums go to the library's
+ * static device scratch instead of the plan's workspace. The scratch is one
+ * fixed array of FFTMV_SCRATCH_BYTES per GPU, held from the library's first
+ * use of a device until the process ends; the call allocates and frees
+ * nothing. Layouts, alignment and ownership of in/out are those of
+ * fftmv_apply / fftmv_apply_adjoint; asynchronous on stream.
+ * Errors: FFTMV_ERR_INVALID_ARG as for the applies (and for dir not 0/1);
+ * FFTMV_ERR_UNSUPPORTED_SIZE when the apply needs more than
+ * FFTMV_SCRATCH_BYTES (the complex spectrum of the transformed side, e.g.
+ * (Nt+1) x Nm complex64 for F in the mixed mask, plus the other side's, in
+ * the precisions of the plan's mask); FFTMV_ERR_HIP if the scratch address
+ * cannot be obtained. Every call on one GPU uses the same scratch, which
+ * keeps the last call's contents: calls that overlap on one GPU (concurrent
+ * streams, host threads) race and must be ordered by the caller. */
+#define FFTMV_SCRATCH_BYTES (128u << 20)
+FFTMV_API int fftmv_apply_scratch(fftmv_plan_t plan, int dir, const double *in, double *out, hipStream_t stream);
+
 /* Free the plan's device memory. Synchronises the device first so that no
  * queued apply still uses it. NULL is accepted. */
 FFTMV_API int fftmv_destroy(fftmv_plan_t plan);
