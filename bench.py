@@ -83,10 +83,15 @@ def parse():
                     help="further warm-up steps, in chunks of 50, while the step time still improves")
     ap.add_argument("--graph-steps", type=int, default=100, help="steps replayed from a HIP graph (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-cols", type=int, default=0, help="oracle sample: input columns (0 = Nm/5)")
+    ap.add_argument("--cpu-sample-cols", type=int, default=0,
+                    help="oracle sample: input columns (0 = all Nm when the host's available memory holds twice "
+                         "the oracle's complex128 Fhat and F, else Nm/5)")
     ap.add_argument("--no-check", action="store_true", help="skip the spot-step check against the oracle")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (reference for the HBM byte counters) and exit")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only measure the memory ceilings (streaming read, copy, the setup transform's pattern) "
+                         "and print them as one JSON line")
     return ap.parse_args()
 
 
@@ -102,6 +107,70 @@ def copy_calibration(mib: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_copy": n * 4, "copies": 3}), flush=True)
+
+
+def memory_ceilings(setup_pattern: bool = False, reps: int = 10):
+    """Memory-system ceilings of this GPU from the plain kernels of
+    libfftmv_ceiling.so (built from fft_block_toeplitz_amd/csrc/ceiling.hip),
+    timed with events on the stream they run on:
+      read_GBs   4 GiB streamed, each workgroup one contiguous 16 or 64 KiB
+                 chunk with all its 16-byte loads in flight (best of both)
+      copy_GBs   2 GiB read and written elsewhere in the same chunks
+                 (read + write bytes per second, best of both)
+      setup_pattern_GBs (optional) the setup transform's memory pattern
+                 without its arithmetic, at 8 and 16 FP64 channels per
+                 workgroup: F [1000][5e5] read in runs of 8 C bytes, 1001
+                 rows of C 8-byte values written (read + write bytes / s)."""
+    import ctypes
+
+    import torch
+
+    from fft_block_toeplitz_amd import build as fbuild
+
+    lib = ctypes.CDLL(fbuild.CEILING_LIB)
+    P = ctypes.c_void_p
+    lib.ceiling_read.argtypes = [P, ctypes.c_size_t, ctypes.c_int, P, P]
+    lib.ceiling_copy.argtypes = [P, P, ctypes.c_size_t, ctypes.c_int, P]
+    lib.ceiling_tile_rw.argtypes = [P, P, ctypes.c_int64, ctypes.c_int, P]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def timed(launch, nbytes):
+        for _ in range(3):
+            assert launch() == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return round(nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+
+    out = {}
+    nbytes = 4 << 30
+    buf = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+    rd = {kib: timed(lambda kib=kib: lib.ceiling_read(buf.data_ptr(), nbytes, kib, sink.data_ptr(), sh), nbytes)
+          for kib in (16, 64)}
+    half = nbytes // 2
+    src, dst = buf.data_ptr(), buf.data_ptr() + half
+    cp = {kib: timed(lambda kib=kib: lib.ceiling_copy(src, dst, half, kib, sh), 2 * half) for kib in (16, 64)}
+    out["read_ceiling_GBs"] = max(rd.values())
+    out["copy_ceiling_GBs"] = max(cp.values())
+    out["read_GBs_by_chunk_kib"] = rd
+    out["copy_GBs_by_chunk_kib"] = cp
+    del buf
+    if setup_pattern:
+        nchan = 500000
+        F = torch.zeros(1000 * nchan, dtype=torch.float64, device="cuda")
+        G = torch.zeros(1001 * nchan, dtype=torch.float64, device="cuda")
+        rw = 8 * nchan * (1000 + 1001)
+        out["setup_pattern_GBs_by_channels"] = {
+            C: timed(lambda C=C: lib.ceiling_tile_rw(F.data_ptr(), G.data_ptr(), nchan, C, sh), rw) for C in (8, 16)}
+        del F, G
+    torch.cuda.empty_cache()
+    return out
 
 
 def elem(mask, direction, s1, s2, cplx):
@@ -127,8 +196,23 @@ def sbgemv_bytes(Nm, Nd, Nt, mask, direction):
     return fhat + K * nin * elem(mask, direction, 2, 3, True) + K * nout * elem(mask, direction, 3, 4, True)
 
 
+def host_mem_bytes():
+    """(MemTotal, MemAvailable) of the host in bytes, or (None, None)."""
+    tot = avail = None
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    tot = int(line.split()[1]) * 1024
+                elif line.startswith("MemAvailable:"):
+                    avail = int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    return tot, avail
+
+
 def host_info():
-    """Host CPU model and the thread settings the oracle runs under."""
+    """Host CPU model, memory and the thread settings the oracle runs under."""
     model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -138,22 +222,25 @@ def host_info():
                     break
     except OSError:
         pass
-    return {"cpu_model": model, "os_cpu_count": os.cpu_count(),
+    tot, avail = host_mem_bytes()
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "mem_total_GB": tot and round(tot / 1e9, 1),
+            "mem_available_GB": avail and round(avail / 1e9, 1),
             "sched_affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
             "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
 
 
 def cpu_baseline(shape, mask, F, m, d, cols):
-    """The FP64 CPU oracle (as it stands) on a column sample of the same
-    workload: Nm reduced to `cols`, everything else unchanged. One F and one
-    F* apply with Fhat precomputed, median of 5 on all the threads the
-    oracle uses and of 3 on one thread; scaled to the full step by the byte
-    model."""
+    """The FP64 CPU oracle (as it stands) on the same workload, or on a
+    column sample of it (Nm reduced to `cols`, everything else unchanged)
+    when cols < Nm. One F and one F* apply with Fhat precomputed, median of
+    5 on all the threads the oracle uses and of 3 on one thread; a sample is
+    scaled to the full step by the byte model."""
     import oracle
 
     Nm, Nd, Nt = shape.Nm, shape.Nd, shape.Nt
-    Fs = np.ascontiguousarray(F[:, :, :cols])
-    ms = np.ascontiguousarray(m[:, :cols])
+    Fs = F if cols >= Nm else np.ascontiguousarray(F[:, :, :cols])
+    ms = m if cols >= Nm else np.ascontiguousarray(m[:, :cols])
+    cols = min(cols, Nm)
     Fh = oracle.setup(Fs)
     sample_bytes = apply_bytes(cols, Nd, Nt, mask, 0) + apply_bytes(cols, Nd, Nt, mask, 1)
 
@@ -175,8 +262,10 @@ def cpu_baseline(shape, mask, F, m, d, cols):
         oracle.set_num_threads(threads)
     gbs = sample_bytes / t / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"F and F* apply at Nm={cols} (of {Nm}), Nd={Nd}, Nt={Nt}, FP64 oracle, Fhat precomputed, "
-                      f"median of 5: {t * 1e3:.1f} ms; GB/s on the step's byte model at that Nm",
+            "sample": (f"F and F* apply at Nm={cols} (of {Nm}), Nd={Nd}, Nt={Nt}, FP64 oracle, Fhat precomputed, "
+                       f"median of 5: {t * 1e3:.1f} ms; GB/s on the step's byte model at that Nm"
+                       + (" (the whole workload)" if cols == Nm else
+                          " (a column sample: the host's available memory is below twice the oracle's Fhat + F)")),
             "ms_per_step_full_equiv": round(t * 1e3 * Nm / cols, 1),
             "one_thread": {"value": round(sample_bytes / t1 / 1e9, 3), "unit": "GB/s",
                            "ms_per_step_full_equiv": round(t1 * 1e3 * Nm / cols, 1)},
@@ -187,6 +276,13 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.read_ceiling:
+        import torch
+
+        torch.cuda.set_device(0)
+        print(json.dumps({"memory_ceilings": memory_ceilings(setup_pattern=True), "peak_GBs": PEAK_HBM_GBS}),
+              flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
@@ -310,6 +406,12 @@ def main():
         kernel[name] = {"avg_ms": round(kms, 5), "bytes": kb, "GB/s": round(kb / (kms * 1e-3) / 1e9, 1)}
     print(f"[bench] kernels {kernel}", file=sys.stderr, flush=True)
 
+    # context: the streaming read and copy ceilings of this GPU, measured
+    # before the extra setups below, whose frees of gigabytes slow HBM-bound
+    # kernels for a while
+    ceilings = memory_ceilings()
+    print(f"[bench] memory ceilings {ceilings}", file=sys.stderr, flush=True)
+
     # correctness spot check against the oracle (direct sum at a few steps)
     check = None
     if not args.no_check:
@@ -343,7 +445,11 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cols = args.cpu_sample_cols or max(1, Nm // 5)
+        cols = args.cpu_sample_cols
+        if not cols:
+            need = (Nt + 1) * Nd * Nm * 16 + Nt * Nd * Nm * 8  # the oracle's Fhat and F
+            avail = host_mem_bytes()[1]
+            cols = Nm if avail is not None and avail >= 2 * need else max(1, Nm // 5)
         t0 = time.perf_counter()
         cpu = cpu_baseline(shape, mask, F, m, d, cols)
         print(f"[bench] cpu baseline {cpu} ({time.perf_counter() - t0:.1f}s)", file=sys.stderr, flush=True)
@@ -388,7 +494,10 @@ def main():
                      "algorithmic_bytes": kn["bytes"]},
         "cpu_baseline": cpu,
         "check": check,
-        "context": {"page_mi355x_f_apply_ms": {"fp64": 1.9, "mixed": 1.3}},
+        "context": {"page_mi355x_f_apply_ms": {"fp64": 1.9, "mixed": 1.3},
+                    "read_ceiling_GBs": ceilings["read_ceiling_GBs"],
+                    "copy_ceiling_GBs": ceilings["copy_ceiling_GBs"],
+                    "dominant_kernel_frac_of_read_ceiling": round(achieved / ceilings["read_ceiling_GBs"], 4)},
         "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
         "setup_s": round(setup_s, 3),
         "setup_ms": {"first": round(setup_s * 1e3, 2), "repeats": [round(x, 2) for x in setup_ms]},

@@ -6,10 +6,7 @@
 
 namespace fftmv {
 
-// Channels per workgroup for a schedule, precision and batch: the widest C
-// that still gives at least 1024 workgroups (four per CU); for small batches
-// the narrowest C (most workgroups). C = 0 when the transform does not fit.
-// Channels per workgroup: the widest tile that still leaves at least
+// Channels per workgroup (C = 0 when the transform does not fit): the widest tile that still leaves at least
 // kMinFftBlocks workgroups (one per CU), else the narrowest tile that fits
 // (small batches). Wide tiles read and write each time step and frequency
 // in runs of C channels, where one channel per workgroup reads every cache

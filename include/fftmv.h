@@ -118,6 +118,10 @@ typedef struct fftmv_plan_s *fftmv_plan_t;
  * FFTMV_FLAG_FHAT_BOTH), the twiddle tables and the workspace, then compute
  * Fhat_k for k = 0..Nt in FP64 on the device (batched real FFT of the Nd*Nm
  * zero-padded series of F) and round it once to each stored precision.
+ * The frequency blocks are the precomputed operator of the page's five
+ * stages (section 1.1): its error bound charges them with the roundoff of
+ * a double-precision transform alone (the c_F eps_d term), which is why
+ * they are computed in FP64 whatever the precision mask. */
  * Returns after the stream has been synchronised.
  *   out     receives the plan; untouched on failure (nothing leaks)
  *   F_dev   device pointer, [Nt][Nd][Nm] FP64, read only, not retained
