@@ -121,7 +121,7 @@ typedef struct fftmv_plan_s *fftmv_plan_t;
  * The frequency blocks are the precomputed operator of the page's five
  * stages (section 1.1): its error bound charges them with the roundoff of
  * a double-precision transform alone (the c_F eps_d term), which is why
- * they are computed in FP64 whatever the precision mask. */
+ * they are computed in FP64 whatever the precision mask.
  * Returns after the stream has been synchronised.
  *   out     receives the plan; untouched on failure (nothing leaks)
  *   F_dev   device pointer, [Nt][Nd][Nm] FP64, read only, not retained
