@@ -1072,7 +1072,12 @@ hipError_t launch_n_row(const SbgemvArgs &a, int64_t nvec, const RowN &rn, hipSt
 
 }  // namespace
 
+// An FP32 GEMV reads its input vector in FP32: the buffer between stages 2
+// and 3 holds the narrower precision of the two, so it is complex64 whenever
+// stage 3 is FP32. The FP32 kernels read 16-byte vectors of two complex64
+// entries; complex128 input there would be misread, so it is rejected.
 hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s) {
+  if (compute_f32 && !a.x_f32) return hipErrorInvalidValue;
   const int nv = compute_f32 ? 2 : 1;
   const int64_t nvec = (a.Nm + nv - 1) / nv;
   const NarrowSplit ns = narrow_split(a.K, a.Nd, nvec);
@@ -1080,7 +1085,7 @@ hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
   if (compute_f32) {
     const RowN rn = row_n(a.K, a.Nd, nvec, resident_c_workgroups());
     if (rn.tpb) {
-      e = a.x_f32 ? launch_n_row<float>(a, nvec, rn, s) : launch_n_row<double>(a, nvec, rn, s);
+      e = launch_n_row<float>(a, nvec, rn, s);
       return e != hipSuccess ? e : hipGetLastError();
     }
   }
@@ -1108,6 +1113,7 @@ hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s)
 }
 
 hipError_t launch_sbgemv_c(const SbgemvArgs &a, bool compute_f32, hipStream_t s) {
+  if (compute_f32 && !a.x_f32) return hipErrorInvalidValue;  // as for launch_sbgemv_n
   const int nv = compute_f32 ? 2 : 1;
   const int64_t nvec = (a.Nm + nv - 1) / nv;
   const TallSplit ts = tall_split(a.K, a.Nd, nvec);
