@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfftmv.so")
 SOURCES = [os.path.join(HERE, "csrc", f)
            for f in ("fft_generic_fwd.hip", "fft_generic_inv.hip", "fft_generic_fwd_blue.hip",
-                     "fft_generic_inv_blue.hip", "fft_fixed_fwd.hip", "fft_fixed_inv.hip", "sbgemv.hip",
+                     "fft_generic_inv_blue.hip", "fft_fixed_fwd.hip", "fft_fixed_inv.hip", "fft_setup.hip", "sbgemv.hip",
                      "padcast.hip", "condition.hip", "scratch.hip", "plan.cpp", "precision.cpp")]
 # measurement kernels of the benchmark (memory ceilings): a library of their own
 CEILING_SRC = os.path.join(HERE, "csrc", "ceiling.hip")

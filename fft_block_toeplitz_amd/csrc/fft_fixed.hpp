@@ -51,10 +51,19 @@ __device__ __forceinline__ int ct_idx(int n, int c) {
   return ct_row(n) * C + c;
 }
 
-template <typename T, int L, int C, int TPB, int P, int S>
+// index of element n of column c in a tile of C columns, padded (above) or not
+template <int C, bool PAD>
+__device__ __forceinline__ int ct_at(int n, int c) {
+  return PAD ? ct_idx<C>(n, c) : n * C + c;
+}
+
+// One Stockham pass (P > 0 has twiddles) over C columns of length-L
+// transforms in LDS. The twiddle table holds w_M^t with M = 2 L TWM (the
+// plan's table of a longer transform when TWM > 1).
+template <typename T, int L, int C, int TPB, int P, int S, int TWM = 1, bool PAD = true>
 __device__ __forceinline__ void ct_lds_pass(cx<T> *lds, const cx<T> *__restrict__ tw) {
   constexpr FftGeom g = make_geometry(L);
-  constexpr int R = g.radix[P], NS = g.ns[P], TWS = g.twstep[P];
+  constexpr int R = g.radix[P], NS = g.ns[P], TWS = g.twstep[P] * TWM;
   constexpr int Lr = L / R, NB = Lr * C, B = (NB + TPB - 1) / TPB;
   cx<T> v[B][R];
 #pragma unroll
@@ -63,7 +72,7 @@ __device__ __forceinline__ void ct_lds_pass(cx<T> *lds, const cx<T> *__restrict_
     if (NB % TPB == 0 || b < NB) {
       const int c = b % C, j = b / C;
 #pragma unroll
-      for (int q = 0; q < R; ++q) v[i][q] = lds[ct_idx<C>(j + q * Lr, c)];
+      for (int q = 0; q < R; ++q) v[i][q] = lds[ct_at<C, PAD>(j + q * Lr, c)];
     }
   }
   __syncthreads();
@@ -77,7 +86,7 @@ __device__ __forceinline__ void ct_lds_pass(cx<T> *lds, const cx<T> *__restrict_
       dft<R, S>(v[i]);
       const int base = (j - k) * R + k;
 #pragma unroll
-      for (int q = 0; q < R; ++q) lds[ct_idx<C>(base + q * NS, c)] = v[i][q];
+      for (int q = 0; q < R; ++q) lds[ct_at<C, PAD>(base + q * NS, c)] = v[i][q];
     }
   }
   __syncthreads();

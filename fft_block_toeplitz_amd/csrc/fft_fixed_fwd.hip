@@ -133,24 +133,13 @@ void launch_fwd_ct_c(const FwdFftArgs &a, const void *tw, hipStream_t s) {
     launch_fwd_ct<T, L, ROUND, Src, 1>(a, tw, s);
 }
 
-// the frequency blocks (setup): FP64 transform, 64-bit offsets, rows of cpr
-// channels. Plain (cached) stores: nothing follows in the same stream that
-// the written lines could slow down, and partial lines of neighbouring
-// tiles merge in L2 instead of reaching HBM twice. At Nt = 1000 the tile
-// holds 8 channels (144 KB of LDS), so every time step of F is read in
-// 64-byte runs; at Nt = 2000 four channels already fill the LDS.
+// the frequency blocks (setup) of small batches: FP64 transform, one channel
+// per workgroup, 64-bit offsets, rows of cpr channels, plain stores (wide
+// batches take the decimation-in-frequency kernel of fft_setup.hip)
 template <int L>
-void launch_fwd_ct_setup(const FwdFftArgs &a, const void *tw, hipStream_t s) {
-  constexpr int C = L == 1000 ? 8 : 4, TPB = 1024;
-  const cx<double> *t = static_cast<const cx<double> *>(tw);
-  if (a.nchan >= kWideBatch) {
-    const int64_t nblocks = (a.nchan + C - 1) / C;
-    hipLaunchKernelGGL((rfft_forward_ct<double, L, C, TPB, false, false, true>), dim3(static_cast<unsigned>(nblocks)),
-                       dim3(TPB), 0, s, a, t, nblocks);
-  } else {
-    hipLaunchKernelGGL((rfft_forward_ct<double, L, 1, kBlock, false, false, true>),
-                       dim3(static_cast<unsigned>(a.nchan)), dim3(kBlock), 0, s, a, t, a.nchan);
-  }
+void launch_fwd_ct_setup_narrow(const FwdFftArgs &a, const void *tw, hipStream_t s) {
+  hipLaunchKernelGGL((rfft_forward_ct<double, L, 1, kBlock, false, false, true>), dim3(static_cast<unsigned>(a.nchan)),
+                     dim3(kBlock), 0, s, a, static_cast<const cx<double> *>(tw), a.nchan);
 }
 
 template <int L>
@@ -179,17 +168,20 @@ bool fwd_ct_applies(const FftGeom &g, const FwdFftArgs &a) {
 
 }  // namespace
 
-bool launch_fft_forward_fixed(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
-                              hipStream_t s) {
+bool launch_fft_forward_fixed(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw, hipStream_t s,
+                              hipError_t *err) {
+  *err = hipSuccess;
   if (!fwd_ct_applies(g, a)) {
     // the frequency blocks: FP64 input and transform, any row structure and size
     const bool setup = has_ct(g.L) && a.Nt == g.L && !a.src_f32 && !a.round_f32 && !compute_f32 &&
                        a.nchan <= a.src_ld && a.cpr >= 1 && grid_fits(a.nchan, kCtItemsPerChannel);
     if (!setup) return false;
-    if (g.L == 1000)
-      launch_fwd_ct_setup<1000>(a, tw, s);
+    if (a.nchan >= kWideBatch)
+      *err = launch_fft_setup_wide(g.L, a, tw, s);
+    else if (g.L == 1000)
+      launch_fwd_ct_setup_narrow<1000>(a, tw, s);
     else
-      launch_fwd_ct_setup<2000>(a, tw, s);
+      launch_fwd_ct_setup_narrow<2000>(a, tw, s);
     return true;
   }
   if (g.L == 1000)

@@ -62,7 +62,9 @@ hipError_t generic_forward(const FftGeom &tile, const FwdFftArgs &a, bool comput
 
 hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s, const BlueTables *blue) {
-  if (!blue && launch_fft_forward_fixed(g, a, compute_f32, tw, s)) return hipGetLastError();
+  hipError_t fixed_err = hipSuccess;
+  if (!blue && launch_fft_forward_fixed(g, a, compute_f32, tw, s, &fixed_err))
+    return fixed_err != hipSuccess ? fixed_err : hipGetLastError();
   const FftGeom &tile = blue ? blue->gM : g;
   const FftLaunch cfg = fft_launch_config(tile, compute_f32, a.nchan);
   if (cfg.C == 0) return hipErrorInvalidValue;

@@ -164,9 +164,13 @@ hipError_t launch_fft_forward(const FftGeom &g, const FwdFftArgs &a, bool comput
 hipError_t launch_fft_inverse(const FftGeom &g, const InvFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s, const BlueTables *blue = nullptr);
 // Fixed-length kernels (fft_fixed_fwd.hip, fft_fixed_inv.hip): launch and return true when one
-// covers this transform, else return false and launch nothing.
-bool launch_fft_forward_fixed(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw,
-                              hipStream_t s);
+// covers this transform (*err: an error found before the launch), else return false and launch
+// nothing.
+bool launch_fft_forward_fixed(const FftGeom &g, const FwdFftArgs &a, bool compute_f32, const void *tw, hipStream_t s,
+                              hipError_t *err);
+// The setup transform of a wide batch (fft_setup.hip): Nt = L = 1000 or 2000, FP64 samples,
+// frequency blocks of cpr-channel rows; tw = w_2L^t, t < 2L, complex128.
+hipError_t launch_fft_setup_wide(int L, const FwdFftArgs &a, const void *tw, hipStream_t s);
 bool launch_fft_inverse_fixed(const FftGeom &g, const InvFftArgs &a, bool compute_f32, const void *tw,
                               hipStream_t s);
 hipError_t launch_sbgemv_n(const SbgemvArgs &a, bool compute_f32, hipStream_t s);

@@ -377,13 +377,16 @@ int setup_impl(fftmv_plan_s *p, const double *F, hipStream_t s) {
   if (!mul_ok(K, Nd, &tmp) || !mul_ok(tmp, p->ldF32, &n32) || !mul_ok(tmp, p->ldF64, &n64) ||
       !mul_ok(n64, 16, &tmp))
     return FFTMV_ERR_OUT_OF_MEMORY;
+  // the transform writes every (row, column < Nm) entry; only the padding
+  // columns Nm..ld-1 of each of the K Nd rows are cleared here
   if (want32) {
     FFTMV_TRY(dev_alloc(p, &p->fhat32, static_cast<size_t>(n32) * 8));
-    FFTMV_TRY(hipMemsetAsync(p->fhat32, 0, static_cast<size_t>(n32) * 8, s));
+    FFTMV_TRY(launch_zero_cols(p->fhat32, K * Nd, p->ldF32 * 8, Nm * 8, (p->ldF32 - Nm) * 8, s));
     p->fhat_bytes += static_cast<size_t>(n32) * 8;
   }
   if (want64) {
     FFTMV_TRY(dev_alloc(p, &p->fhat64, static_cast<size_t>(n64) * 16));
+    FFTMV_TRY(launch_zero_cols(p->fhat64, K * Nd, p->ldF64 * 16, Nm * 16, (p->ldF64 - Nm) * 16, s));
     p->fhat_bytes += static_cast<size_t>(n64) * 16;
   }
 
