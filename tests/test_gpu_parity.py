@@ -210,6 +210,10 @@ def test_random_shapes_match_oracle(fm, rc):
                                    (37, 111, 1000),   # wide batch, odd rows: channel pairs straddle rows
                                    (33, 7, 2000),     # narrow batch, Nt = 2000
                                    (2048, 2, 2000),   # wide batch, Nt = 2000, 256-byte aligned rows
+                                   (1001, 3, 2000),   # wide batch, Nt = 2000: ragged 8-channel tile, odd rows
+                                   (512, 1, 1000),    # the smallest wide batch, Nt = 1000
+                                   (513, 1, 1000),    # one channel past a 16-channel tile
+                                   (31, 17, 1000),    # 527 channels: odd rows of 31, ragged tile
                                    (9, 4, 21),        # radix 3 and 7
                                    (9, 4, 13)])       # Bluestein form
 def test_fhat_matches_oracle(fm, shape):
